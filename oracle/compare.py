@@ -1,0 +1,58 @@
+"""Acceptance criteria for GPU results against the oracle (test infrastructure).
+
+Random-input floating-point results pass when both hold:
+  * normwise:    ||C - T||_F / ||T||_F <= 1e-3
+  * elementwise: |C_ij - T_ij| <= 1e-2 * scale_ij + 1e-3,
+    scale_ij = |alpha| * U_ij + |beta| * |C_old_ij| (+ |bias_j| when present),
+    with U_ij = sum_k |A_ik||B_kj| from the oracle.
+Integer-valued runs and the q4 dequant must match the oracle's rounded bits
+exactly.  T is the oracle's binary64 result before output rounding.
+"""
+import numpy as np
+
+NORMWISE_TOL = 1e-3
+ELEM_RTOL = 1e-2
+ELEM_ATOL = 1e-3
+
+
+def normwise_rel_err(C, T):
+    C = np.asarray(C, dtype=np.float64)
+    T = np.asarray(T, dtype=np.float64)
+    den = np.linalg.norm(T)
+    num = np.linalg.norm(C - T)
+    if den == 0.0:
+        return 0.0 if num == 0.0 else np.inf
+    return float(num / den)
+
+
+def elem_scale(U, alpha=1.0, beta=0.0, C_old=None, bias=None):
+    s = abs(alpha) * np.asarray(U, dtype=np.float64)
+    if beta != 0.0 and C_old is not None:
+        s = s + abs(beta) * np.abs(np.asarray(C_old, dtype=np.float64))
+    if bias is not None:
+        s = s + np.abs(np.asarray(bias, dtype=np.float64))[None, :]
+    return s
+
+
+def elem_violations(C, T, scale, rtol=ELEM_RTOL, atol=ELEM_ATOL):
+    C = np.asarray(C, dtype=np.float64)
+    T = np.asarray(T, dtype=np.float64)
+    bad = ~(np.abs(C - T) <= rtol * scale + atol)
+    return int(np.count_nonzero(bad))
+
+
+def check_tolerance(C, T, scale, normwise_tol=NORMWISE_TOL):
+    """Returns (ok, report) for the floating-point acceptance criteria."""
+    nre = normwise_rel_err(C, T)
+    nbad = elem_violations(C, T, scale)
+    finite = bool(np.all(np.isfinite(np.asarray(C, dtype=np.float64))))
+    ok = finite and nre <= normwise_tol and nbad == 0
+    return ok, {"normwise_rel_err": nre, "elem_violations": nbad, "finite": finite}
+
+
+def bits_mismatch(got_bits, want_bits):
+    """Number of positions whose raw bits differ (NaN never expected here)."""
+    got = np.asarray(got_bits)
+    want = np.asarray(want_bits)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    return int(np.count_nonzero(got != want))

@@ -1,0 +1,77 @@
+"""Pins for the oracle's q4 dequantisation and the prefill composition.
+
+* the hand-derived blocks in tests/golden/q4_blocks.txt (nibble order, scale
+  position and byte order, signed zero, subnormals, overflow, ties-to-even);
+* every binary16 scale bit pattern times every code, against numpy's
+  binary16 cast of the exact product;
+* multi-row, multi-block addressing against a per-block decode;
+* prefill with unit scales, where W16 holds the integers q-8 and the product
+  must equal an int64 matmul exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_engineering_amd import inputs
+from golden_io import q4_blocks
+
+
+@pytest.mark.parametrize("name,block,want", list(q4_blocks()))
+def test_golden_blocks(name, block, want):
+    got = oracle.dequant_q4(block, 1, 32)
+    assert np.array_equal(got[0], want), name
+
+
+def _all_scales_blocks():
+    scales = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    codes = np.empty((65536, 1, 32), dtype=np.uint8)
+    codes[:, 0, :16] = np.arange(16)
+    codes[:, 0, 16:] = np.arange(15, -1, -1)
+    return scales, codes
+
+
+def test_exhaustive_scales_times_codes():
+    scales, codes = _all_scales_blocks()
+    q = inputs.pack_q4(scales[:, None], codes)
+    got = oracle.dequant_q4(q, 65536, 32)
+    d = scales.view(np.float16).astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        want = (d[:, None] * (codes[:, 0, :].astype(np.float64) - 8.0)).astype(np.float16)
+    fin = np.isfinite(d)
+    assert np.array_equal(got[fin], want.view(np.uint16)[fin])
+    # non-finite scales: the class (NaN / signed inf) must agree
+    g = got[~fin].view(np.float16).astype(np.float64)
+    w = want[~fin].astype(np.float64)
+    assert np.array_equal(np.isnan(g), np.isnan(w))
+    nn = ~np.isnan(w)
+    assert np.array_equal(g[nn], w[nn])
+
+
+def test_multirow_addressing():
+    rows, cols = 7, 96
+    q = inputs.q4_weights(rows, cols, config=90)
+    got = oracle.dequant_q4(q, rows, cols)
+    blk = q.reshape(rows, cols // 32, 18)
+    for r in range(rows):
+        for b in range(cols // 32):
+            one = oracle.dequant_q4(blk[r, b], 1, 32)[0]
+            assert np.array_equal(got[r, 32 * b:32 * b + 32], one)
+
+
+def test_rejects_ragged_cols():
+    with pytest.raises(ValueError):
+        oracle.dequant_q4(np.zeros(18, np.uint8), 1, 16)
+
+
+def test_prefill_unit_scale_exact():
+    M, N, K = 33, 70, 256  # the tail shape the prefill page tests with
+    r = np.random.Generator(np.random.PCG64(700))
+    codes = r.integers(0, 16, (N, K // 32, 32))
+    scales = np.full((N, K // 32), 0x3C00, dtype=np.uint16)  # d = 1.0
+    q = inputs.pack_q4(scales, codes)
+    Ai = r.integers(-4, 5, (M, K))
+    A = inputs.to_bits(Ai.astype(float), "f16")
+    T, U, W16 = oracle.prefill(A, q, N, K)
+    Wi = codes.reshape(N, K).astype(np.int64) - 8
+    assert np.array_equal(W16.view(np.float16).astype(np.int64), Wi)
+    assert np.array_equal(T, (Ai @ Wi.T).astype(float))
