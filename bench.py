@@ -1,0 +1,297 @@
+"""Benchmark of the dense-GEMM hot path on one MI355X.
+
+One step is one fp16 GEMM C = A @ B at M = N = K = 4096 (row-major A and B,
+fp16 output, fp32 accumulation, alpha = 1, beta = 0) through the C ABI.
+Prints ONE JSON line: TFLOP/s of that GEMM (whole job, one GPU), the
+roofline of its kernel (algorithmic FLOPs over the kernel's average duration,
+measured with HIP events on the stream it is launched on, against the
+2.5 PFLOP/s dense fp16 MFMA peak), the CPU oracle timed on a bounded sample
+of the same product, and the other workloads' figures: the 2048-token q4
+prefill projections in tokens/s (dequant per call and GEMM only), the fp32
+ladder, and the tall-skinny fused-epilogue shapes as HBM roofline fractions.
+
+Inputs are synthetic and seeded (dense_gemm_engineering_amd.inputs); they are
+resident in HBM before any timed region starts.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # TFLOP/s, dense MFMA
+HBM_PEAK_GBS = 8000.0
+
+# ------------------------------------------------------------ accounting
+
+def gemm_flops(M, N, K):
+    """2MNK: one multiply and one add per term of every dot product."""
+    return 2.0 * M * N * K
+
+
+def gemm_alg_bytes(M, N, K, s_in, s_out, beta_read=False, bias_bytes=0):
+    """Least traffic any kernel can have: read A and B once, write C once
+    (plus C's old value when beta != 0, plus the bias vector)."""
+    b = s_in * (M * K + K * N) + s_out * M * N + bias_bytes
+    if beta_read:
+        b += s_out * M * N
+    return float(b)
+
+
+def ideal_intensity(M, N, K, s):
+    """Best-case FLOP/byte of an M x K by K x N product with s-byte numbers."""
+    return gemm_flops(M, N, K) / (s * (M * K + K * N + M * N))
+
+
+def dequant_alg_bytes(rows, cols):
+    """q4 -> fp16: 18 bytes per 32 weights read, 2 bytes per weight written."""
+    return rows * cols / 32 * 18 + rows * cols * 2.0
+
+
+def prefill_stack_tokens_per_s(t_attn, t_up, t_down, tokens=2048, layers=32):
+    """tokens / (layers x [4 square projections + 2 up-projections + 1 down]).
+
+    A 7B-like decoder layer with hidden 4096 and FFN 11008 has four 4096 x 4096
+    projections (q, k, v, o), two 11008 x 4096 (gate, up) and one 4096 x 11008
+    (down): 6.5e9 projection weights over 32 layers."""
+    return tokens / (layers * (4 * t_attn + 2 * t_up + t_down))
+
+
+# ------------------------------------------------------------ timing
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn warmup times, then time `steps` calls.  Returns (per-call
+    durations in s from event pairs around each call, wall of the whole
+    bracket in s).  All on torch's current stream, which the binding uses."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) * 1e-3 for s, e in ev]
+    return per, wall
+
+
+def _src_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_engineering_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip", ".cpp", ".inc")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.md" % kernel_key)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith("- "):
+                k, v = line.strip()[2:].split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != _src_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------ workloads
+
+def _dev(bits, dtype, torch):
+    bits = np.ascontiguousarray(bits)
+    if dtype == "f32":
+        return torch.from_numpy(bits.view(np.int32).copy()).view(torch.float32).cuda()
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return torch.from_numpy(bits.view(np.int16).copy()).view(tdt).cuda()
+
+
+def _med(x):
+    return float(np.median(x))
+
+
+def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
+    """Per shape: dequant (HBM-cold by rotating weight sets), GEMM, tok/s."""
+    out = {}
+    for shape in ("up", "attn", "down"):
+        A, q, N, K = inputs.cfg4(shape)
+        dA = _dev(A, "f16", torch)
+        nset = max(1, int(np.ceil(rotate_bytes / dequant_alg_bytes(N, K))))
+        qs = [torch.from_numpy(q).cuda() for _ in range(nset)]
+        ws = [torch.empty((N, K), dtype=torch.float16, device="cuda") for _ in range(nset)]
+        C = torch.empty((2048, N), dtype=torch.float16, device="cuda")
+        wsz = dge.gemm_workspace_size(2048, N, K, torch.float16)
+        work = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda") if wsz else None
+        it = [0]
+
+        def deq():
+            i = it[0] % nset
+            it[0] += 1
+            dge.dequant_q4_f16(qs[i], N, K, out=ws[i])
+
+        def gem():
+            dge.gemm_f16(dA, ws[0], C, trans_b=True, workspace=work)
+
+        t_deq, _ = time_launches(deq, steps, 3, torch)
+        t_gem, _ = time_launches(gem, steps, 3, torch)
+        td, tg = _med(t_deq), _med(t_gem)
+        out[shape] = {"N": N, "K": K, "dequant_us": td * 1e6, "gemm_us": tg * 1e6,
+                      "dequant_GBs": dequant_alg_bytes(N, K) / td / 1e9,
+                      "dequant_hbm_frac": dequant_alg_bytes(N, K) / td / 1e9 / HBM_PEAK_GBS,
+                      "gemm_TFLOPs": gemm_flops(2048, N, K) / tg / 1e12,
+                      "gemm_mfma_frac": gemm_flops(2048, N, K) / tg / 1e12 / PEAK["f16"],
+                      "tok_s_dequant_per_call": 2048 / (td + tg),
+                      "tok_s_gemm_only": 2048 / tg}
+        del qs, ws, C, work, dA
+    t = {k: (out[k]["dequant_us"] + out[k]["gemm_us"]) * 1e-6 for k in out}
+    g = {k: out[k]["gemm_us"] * 1e-6 for k in out}
+    out["stack_7b_like"] = {
+        "tok_s_dequant_per_call": prefill_stack_tokens_per_s(t["attn"], t["up"], t["down"]),
+        "tok_s_gemm_only": prefill_stack_tokens_per_s(g["attn"], g["up"], g["down"])}
+    return out
+
+
+def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
+    out = {}
+    for N in (160, 32):
+        X, W, bias = inputs.cfg5(N)
+        alg = gemm_alg_bytes(65536, N, 160, 2, 2, bias_bytes=2 * N)
+        nset = max(1, int(np.ceil(rotate_bytes / alg)))
+        Xs = [_dev(X, "f16", torch) for _ in range(nset)]
+        Cs = [torch.empty((65536, N), dtype=torch.float16, device="cuda") for _ in range(nset)]
+        dW, db = _dev(W, "f16", torch), _dev(bias, "f16", torch)
+        it = [0]
+
+        def run():
+            i = it[0] % nset
+            it[0] += 1
+            dge.gemm_f16(Xs[i], dW, Cs[i], epi="bias_gelu", bias=db)
+
+        per, _ = time_launches(run, steps, 3, torch)
+        t = _med(per)
+        out["N%d" % N] = {"us": t * 1e6, "GBs": alg / t / 1e9, "hbm_frac": alg / t / 1e9 / HBM_PEAK_GBS,
+                          "TFLOPs": gemm_flops(65536, N, 160) / t / 1e12}
+        del Xs, Cs
+    return out
+
+
+def bench_ladder(dge, inputs, torch, steps):
+    out = {}
+    for n in (1024, 2048, 4096):
+        A, B = inputs.cfg3(n)
+        dA, dB = _dev(A, "f32", torch), _dev(B, "f32", torch)
+        C = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        row = {}
+        algos = ["naive", "lds_tiled", "mfma"] if n <= 2048 else ["lds_tiled", "mfma"]
+        for algo in algos:
+            s = max(2, steps // 10) if algo != "mfma" else steps
+            per, _ = time_launches(lambda: dge.gemm_ex(dA, dB, C, algo=algo), s, 1, torch)
+            t = _med(per)
+            row[algo] = {"us": t * 1e6, "TFLOPs": gemm_flops(n, n, n) / t / 1e12,
+                         "fp32_mfma_frac": gemm_flops(n, n, n) / t / 1e12 / PEAK["f32"]}
+        out["n%d" % n] = row
+    return out
+
+
+def cpu_baseline(A, B, seconds_target=15.0):
+    """The oracle, untuned, on all host cores: rows of the 4096^3 product."""
+    import oracle
+    cores = oracle.default_threads()
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.gemm(A[:rows], B, "f16", want_U=False, threads=cores)
+    t = time.perf_counter() - t0
+    # scale the sample so the measured leg takes about seconds_target
+    rows = int(min(4096, max(rows, rows * seconds_target / max(t, 1e-3))))
+    rows = max(cores, rows - rows % cores)
+    t0 = time.perf_counter()
+    oracle.gemm(A[:rows], B, "f16", want_U=False, threads=cores)
+    t = time.perf_counter() - t0
+    return {"value": gemm_flops(rows, 4096, 4096) / t / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": t,
+            "sample": "rows 0..%d of the 4096^3 fp16 product (%.2f GFLOP), binary64 "
+                      "accumulation, row-parallel over %d threads" % (rows - 1, gemm_flops(rows, 4096, 4096) / 1e9, cores)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline GEMM")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_gemm_engineering_amd.binding as dge
+    from dense_gemm_engineering_amd import inputs
+
+    dge.gemm_init()
+    M = N = K = 4096
+    A, B = inputs.cfg2(args.dtype)
+    dA, dB = _dev(A, args.dtype, torch), _dev(B, args.dtype, torch)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    wsz = dge.gemm_workspace_size(M, N, K, dA.dtype)
+    work = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda") if wsz else None
+    fn = (lambda: dge.gemm_f16(dA, dB, C, workspace=work)) if args.dtype == "f16" else \
+        (lambda: dge.gemm_bf16(dA, dB, C, workspace=work))
+
+    per, wall = time_launches(fn, args.steps, args.warmup, torch)
+    flops = gemm_flops(M, N, K)
+    avg_kernel = float(np.mean(per))
+    ms_per_step = wall / args.steps * 1e3
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / avg_kernel / 1e12
+    traffic = _traffic("gemm_%s_4096" % args.dtype)
+    line = {
+        "metric": "TFLOP/s fp16 GEMM 4096^3 (% of MFMA peak); 2K-token prefill GEMM tok/s",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": "%s GEMM M=N=K=4096, row-major A (MxK) and B (KxN), entries "
+                               "N(0,1)/sqrt(K), fp32 accumulate, fp16 output, alpha=1, beta=0"
+                               % args.dtype, "M": M, "N": N, "K": K, "accumulate": "f32",
+                   "output": "f16", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[args.dtype],
+                     "unit": "TFLOP/s", "frac": achieved / PEAK[args.dtype],
+                     "traffic": traffic,
+                     "kernel_us_mean": avg_kernel * 1e6, "kernel_us_median": _med(per) * 1e6,
+                     "alg_bytes": gemm_alg_bytes(M, N, K, 2, 2)},
+    }
+    if not args.no_extra:
+        extra_steps = max(10, min(args.steps, 30))
+        line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps)
+        line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps)
+        line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,442 @@
+// C ABI of the gfx950 dense-GEMM library: argument validation, kernel and
+// schedule selection, launches on the caller's stream.  Declarations and the
+// contract of every entry point are in include/gemm.h.
+#include "gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "launch.h"
+
+namespace {
+
+using namespace dge;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int ok;       // 1 = gfx950, usable
+    int cus;      // compute units
+};
+
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+
+gemm_status_t current_device(DeviceInfo* out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return GEMM_ERR_DEVICE;
+    }
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        DeviceInfo info{0, 0};
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+            std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+            info.ok = 1;
+            info.cus = prop.multiProcessorCount;
+        }
+        (void)hipGetLastError();
+        g_dev[dev] = info;
+    });
+    if (!g_dev[dev].ok) return GEMM_ERR_DEVICE;
+    *out = g_dev[dev];
+    return GEMM_OK;
+}
+
+// GEMM_TEST_FAIL=<site>: force an error after validation, before any launch.
+gemm_status_t forced_failure() {
+    const char* f = std::getenv("GEMM_TEST_FAIL");
+    if (!f || !*f) return GEMM_OK;
+    if (!std::strcmp(f, "launch")) return GEMM_ERR_LAUNCH;
+    if (!std::strcmp(f, "device")) return GEMM_ERR_DEVICE;
+    if (!std::strcmp(f, "workspace")) return GEMM_ERR_WORKSPACE;
+    return GEMM_OK;
+}
+
+int in_bytes(int dt) { return dt == IN_F32 ? 4 : 2; }
+int out_bytes(int ct) { return ct == OUT_F32 ? 4 : 2; }
+
+// Byte range [lo, hi) spanned by a rows x cols matrix with leading dimension ld.
+struct Range {
+    uintptr_t lo, hi;
+};
+Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int elem) {
+    if (!p || rows <= 0 || cols <= 0) return {0, 0};
+    uintptr_t lo = (uintptr_t)p;
+    return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
+}
+bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+struct Gemm {
+    int dt;
+    int64_t M, N, K;
+    float alpha, beta;
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    int trans_b;
+    void* C;
+    int64_t ldc;
+    int c_type;
+    int epi;
+    const void* bias;
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+gemm_status_t validate(const Gemm& g) {
+    if (g.dt < IN_F16 || g.dt > IN_F32) return GEMM_ERR_INVALID_VALUE;
+    if (g.c_type < OUT_F32 || g.c_type > OUT_BF16) return GEMM_ERR_INVALID_VALUE;
+    if (g.dt == IN_F32 && g.c_type != OUT_F32) return GEMM_ERR_INVALID_VALUE;
+    if (g.epi < EPI_NONE || g.epi > EPI_BIAS_GELU) return GEMM_ERR_INVALID_VALUE;
+    if (g.trans_b != 0 && g.trans_b != 1) return GEMM_ERR_INVALID_VALUE;
+    if (g.M < 0 || g.N < 0 || g.K < 0) return GEMM_ERR_INVALID_VALUE;
+    if (g.M > kMaxDim || g.N > kMaxDim || g.K > kMaxDim) return GEMM_ERR_INVALID_VALUE;
+    if (!std::isfinite(g.alpha) || !std::isfinite(g.beta)) return GEMM_ERR_INVALID_VALUE;
+    if (g.M == 0 || g.N == 0) return GEMM_OK;
+    if (g.ldc < g.N || g.ldc > kMaxDim * 64) return GEMM_ERR_INVALID_VALUE;
+    if (g.lda < std::max<int64_t>(1, g.K) || g.lda > kMaxDim * 64) return GEMM_ERR_INVALID_VALUE;
+    const int64_t ldb_min = g.trans_b ? std::max<int64_t>(1, g.K) : g.N;
+    if (g.ldb < ldb_min || g.ldb > kMaxDim * 64) return GEMM_ERR_INVALID_VALUE;
+    // offsets must fit the kernels' 64-bit element indexing with margin
+    if ((double)g.M * (double)g.ldc > 9e15 || (double)g.M * (double)g.lda > 9e15 ||
+        (double)(g.trans_b ? g.N : g.K) * (double)g.ldb > 9e15)
+        return GEMM_ERR_INVALID_VALUE;
+    if (!g.C) return GEMM_ERR_INVALID_VALUE;
+    if (g.K > 0 && (!g.A || !g.B)) return GEMM_ERR_INVALID_VALUE;
+    if (g.epi != EPI_NONE && !g.bias) return GEMM_ERR_INVALID_VALUE;
+    const Range rc = span(g.C, g.M, g.N, g.ldc, out_bytes(g.c_type));
+    const Range ra = g.K > 0 ? span(g.A, g.M, g.K, g.lda, in_bytes(g.dt)) : Range{0, 0};
+    const Range rb = g.K > 0 ? (g.trans_b ? span(g.B, g.N, g.K, g.ldb, in_bytes(g.dt))
+                                          : span(g.B, g.K, g.N, g.ldb, in_bytes(g.dt)))
+                             : Range{0, 0};
+    const Range rbias = g.epi != EPI_NONE ? span(g.bias, 1, g.N, g.N, in_bytes(g.dt)) : Range{0, 0};
+    if (overlaps(rc, ra) || overlaps(rc, rb) || overlaps(rc, rbias)) return GEMM_ERR_INVALID_VALUE;
+    return GEMM_OK;
+}
+
+Epilogue make_epilogue(const Gemm& g) {
+    Epilogue e;
+    e.alpha = g.alpha;
+    e.beta = g.beta;
+    e.epi = g.epi;
+    e.bias = g.bias;
+    return e;
+}
+
+SimpleArgs simple_args(const Gemm& g) {
+    SimpleArgs a;
+    a.A = g.A;
+    a.B = g.B;
+    a.C = g.C;
+    a.lda = g.lda;
+    a.ldb = g.ldb;
+    a.ldc = g.ldc;
+    a.M = (int)g.M;
+    a.N = (int)g.N;
+    a.K = (int)g.K;
+    a.trans_b = g.trans_b;
+    a.c_type = g.c_type;
+    a.ep = make_epilogue(g);
+    return a;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Relative MFMA throughput of each tile when the chip is full (the bigger
+// the per-wave tile, the more MFMAs each LDS byte feeds), and how many of
+// its workgroups one CU holds.
+double tile_efficiency(int tile) {
+    switch (tile) {
+        case TILE_256x256: return 1.0;
+        case TILE_256x128: return 0.9;
+        case TILE_128x128: return 0.75;
+        default: return 0.55;
+    }
+}
+int tile_occupancy(int tile) { return tile == TILE_256x256 || tile == TILE_256x128 ? 1 : 2; }
+
+// Pick the tile that minimises (rounds of workgroups) x (tile work) / efficiency.
+int choose_tile(int64_t M, int64_t N, int cus) {
+    int best = TILE_256x256;
+    double best_cost = 1e300;
+    for (int t = TILE_256x256; t <= TILE_128x64; ++t) {
+        const TileShape ts = tile_shape(t);
+        const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+        const int64_t slots = (int64_t)cus * tile_occupancy(t);
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double cost = (double)rounds * ts.bm * ts.bn / tile_efficiency(t);
+        if (cost < best_cost * 0.999) {
+            best_cost = cost;
+            best = t;
+        }
+    }
+    return best;
+}
+
+// Split K when the tiles cannot fill the chip and each slice still has
+// enough K to amortise its prologue and the fixup pass.
+int choose_splits(int64_t M, int64_t N, int64_t K, int tile, int dt, int cus) {
+    const TileShape ts = tile_shape(tile);
+    const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+    const int64_t slots = (int64_t)cus * tile_occupancy(tile);
+    if (tiles * 2 > slots) return 1;
+    int s = (int)std::min<int64_t>(slots / tiles, 8);
+    const int64_t min_k = 16 * stage_k(dt);
+    while (s > 1 && K / s < min_k) --s;
+    return std::max(s, 1);
+}
+
+size_t ws_bytes_for(int64_t M, int64_t N, int splits) {
+    return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+gemm_status_t launch_status(hipError_t e) {
+    if (e == hipSuccess) return GEMM_OK;
+    return GEMM_ERR_LAUNCH;
+}
+
+gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus) {
+    if (tile == GEMM_TILE_AUTO) tile = choose_tile(g.M, g.N, cus);
+    if (tile < TILE_256x256 || tile > TILE_128x64) return GEMM_ERR_INVALID_VALUE;
+    const TileShape ts = tile_shape(tile);
+    const int bk = stage_k(g.dt);
+    const int max_splits = std::max(1, ceil_div(g.K, bk));
+    bool explicit_split = splits > 1;
+    if (splits == 0) splits = choose_splits(g.M, g.N, g.K, tile, g.dt, cus);
+    if (splits > max_splits) splits = max_splits;
+    if (splits > 1) {
+        const size_t need = ws_bytes_for(g.M, g.N, splits);
+        if (!g.ws || g.ws_bytes < need || !aligned16(g.ws)) {
+            if (explicit_split) return GEMM_ERR_WORKSPACE;
+            splits = 1;
+        }
+    }
+    MfmaArgs a;
+    a.A = g.A;
+    a.B = g.B;
+    a.C = g.C;
+    a.ws = splits > 1 ? (float*)g.ws : nullptr;
+    a.lda = g.lda;
+    a.ldb = g.ldb;
+    a.ldc = g.ldc;
+    a.M = (int)g.M;
+    a.N = (int)g.N;
+    a.K = (int)g.K;
+    a.tiles_m = ceil_div(g.M, ts.bm);
+    a.tiles_n = ceil_div(g.N, ts.bn);
+    a.splits = splits;
+    // K slices are whole stages
+    const int stages = ceil_div(g.K, bk);
+    a.k_per_split = splits > 1 ? ceil_div(stages, splits) * bk : (int)std::max<int64_t>(g.K, 1);
+    if (splits > 1) a.splits = ceil_div(g.K, a.k_per_split);
+    splits = a.splits;
+    const int per_xcd = std::max(1, (a.tiles_m * a.tiles_n) / 8);
+    int gm = 1;
+    while (gm * gm * 2 < per_xcd) gm *= 2;
+    a.group_m = std::max(1, std::min(env_int("GEMM_GROUP_M", gm), a.tiles_m));
+    a.c_type = g.c_type;
+    const int vec_el = 16 / in_bytes(g.dt);
+    const bool vec = aligned16(g.A) && aligned16(g.B) && aligned16(g.C) && g.lda % vec_el == 0 &&
+                     g.ldb % vec_el == 0 && (g.ldc * out_bytes(g.c_type)) % 16 == 0;
+    a.vec_ok = vec ? 1 : 0;
+    a.ep = make_epilogue(g);
+    const bool fast = vec && g.M % ts.bm == 0 && g.N % ts.bn == 0 && g.K % bk == 0 &&
+                      (splits == 1 || a.k_per_split % bk == 0);
+    const int64_t nwg = (int64_t)a.tiles_m * a.tiles_n * splits;
+    if (nwg > 0x7fffffff) return GEMM_ERR_NOT_SUPPORTED;
+    hipError_t e;
+    switch (g.dt) {
+        case IN_F16: e = launch_mfma_f16(tile, g.trans_b, fast, a, (int)nwg, g.stream); break;
+        case IN_BF16: e = launch_mfma_bf16(tile, g.trans_b, fast, a, (int)nwg, g.stream); break;
+        default: e = launch_mfma_f32(tile, g.trans_b, fast, a, (int)nwg, g.stream); break;
+    }
+    if (e != hipSuccess) return launch_status(e);
+    if (splits > 1) e = launch_splitk_fixup(g.dt, simple_args(g), (const float*)g.ws, splits, g.stream);
+    return launch_status(e);
+}
+
+gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
+    gemm_status_t st = validate(g);
+    if (st != GEMM_OK) return st;
+    gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
+    if (tuning) tn = *tuning;
+    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_MFMA) return GEMM_ERR_INVALID_VALUE;
+    if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_128x64) return GEMM_ERR_INVALID_VALUE;
+    if (tn.splits < 0) return GEMM_ERR_INVALID_VALUE;
+    if (g.M == 0 || g.N == 0) return GEMM_OK;
+    if ((st = forced_failure()) != GEMM_OK) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    switch (tn.algo) {
+        case GEMM_ALGO_NAIVE:
+            if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
+            return launch_status(launch_naive(g.dt, simple_args(g), g.stream));
+        case GEMM_ALGO_LDS_TILED:
+            if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
+            return launch_status(launch_lds_tiled(g.dt, simple_args(g), g.stream));
+        default:
+            return run_mfma(g, tn.tile, tn.splits, dev.cus);
+    }
+}
+
+Gemm make_gemm(int dt, int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+               const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+               gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    Gemm g;
+    g.dt = dt;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.A = A;
+    g.lda = lda;
+    g.B = B;
+    g.ldb = ldb;
+    g.trans_b = trans_b;
+    g.C = C;
+    g.ldc = ldc;
+    g.c_type = (int)c_type;
+    g.epi = (int)epi;
+    g.bias = bias;
+    g.ws = workspace;
+    g.ws_bytes = workspace_bytes;
+    g.stream = (hipStream_t)stream;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+                       gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return run_gemm(make_gemm(IN_F16, M, N, K, alpha, A, lda, B, ldb, trans_b, beta, C, ldc, c_type,
+                              epi, bias, workspace, workspace_bytes, stream),
+                    nullptr);
+}
+
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+                        gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return run_gemm(make_gemm(IN_BF16, M, N, K, alpha, A, lda, B, ldb, trans_b, beta, C, ldc,
+                              c_type, epi, bias, workspace, workspace_bytes, stream),
+                    nullptr);
+}
+
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+                       gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return run_gemm(make_gemm(IN_F32, M, N, K, alpha, A, lda, B, ldb, trans_b, beta, C, ldc, c_type,
+                              epi, bias, workspace, workspace_bytes, stream),
+                    nullptr);
+}
+
+gemm_status_t gemm_ex(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float alpha,
+                      const void* A, int64_t lda, const void* B, int64_t ldb, int trans_b,
+                      float beta, void* C, int64_t ldc, gemm_out_t c_type, gemm_epilogue_t epi,
+                      const void* bias, void* workspace, size_t workspace_bytes,
+                      const gemm_tuning_t* tuning, void* stream) {
+    return run_gemm(make_gemm((int)in_type, M, N, K, alpha, A, lda, B, ldb, trans_b, beta, C, ldc,
+                              c_type, epi, bias, workspace, workspace_bytes, stream),
+                    tuning);
+}
+
+gemm_status_t dequant_q4_f16(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
+                             void* stream) {
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || ldo < cols) return GEMM_ERR_INVALID_VALUE;
+    if (rows > kMaxDim || cols > kMaxDim || ldo > kMaxDim * 64) return GEMM_ERR_INVALID_VALUE;
+    if (rows == 0 || cols == 0) return GEMM_OK;
+    if (!q || !out || ((uintptr_t)q & 1) || ((uintptr_t)out & 1)) return GEMM_ERR_INVALID_VALUE;
+    const Range rq = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(rows * (cols / 32) * 18)};
+    if (overlaps(rq, span(out, rows, cols, ldo, 2))) return GEMM_ERR_INVALID_VALUE;
+    gemm_status_t st = forced_failure();
+    if (st != GEMM_OK) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    const int vec_out = aligned16(out) && ldo % 8 == 0;
+    return launch_status(
+        launch_dequant_q4(q, out, rows, cols, ldo, vec_out, (hipStream_t)stream));
+}
+
+gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* q, void* w16, void* C, int64_t ldc, gemm_out_t c_type,
+                             gemm_epilogue_t epi, const void* bias, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return GEMM_ERR_INVALID_VALUE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (K > 0 && (!q || !w16)) return GEMM_ERR_INVALID_VALUE;
+    // validate the GEMM half before enqueueing the dequant
+    Gemm g = make_gemm(IN_F16, M, N, K, 1.0f, A, lda, w16, std::max<int64_t>(K, 1), 1, 0.0f, C, ldc,
+                       c_type, epi, bias, workspace, workspace_bytes, stream);
+    gemm_status_t st = validate(g);
+    if (st != GEMM_OK) return st;
+    if (K > 0) {
+        const Range rw = span(w16, N, K, K, 2);
+        const Range rq = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(N * (K / 32) * 18)};
+        if (overlaps(rw, rq) || overlaps(rw, span(A, M, K, lda, 2)) ||
+            overlaps(rw, span(C, M, N, ldc, out_bytes((int)c_type))))
+            return GEMM_ERR_INVALID_VALUE;
+        st = dequant_q4_f16(q, w16, N, K, K, stream);
+        if (st != GEMM_OK) return st;
+    }
+    return run_gemm(g, nullptr);
+}
+
+size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {
+    if (M <= 0 || N <= 0 || K <= 0 || dtype < IN_F16 || dtype > IN_F32) return 0;
+    DeviceInfo dev{1, 256};
+    if (current_device(&dev) != GEMM_OK) dev.cus = 256;
+    const int tile = choose_tile(M, N, dev.cus);
+    int s = choose_splits(M, N, K, tile, dtype, dev.cus);
+    return ws_bytes_for(M, N, s);
+}
+
+size_t gemm_workspace_size_splits(int64_t M, int64_t N, int splits) {
+    if (M <= 0 || N <= 0 || splits <= 1) return 0;
+    return ws_bytes_for(M, N, splits);
+}
+
+const char* gemm_status_string(gemm_status_t s) {
+    switch (s) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE: invalid argument";
+        case GEMM_ERR_NOT_SUPPORTED: return "GEMM_ERR_NOT_SUPPORTED: request not supported";
+        case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: workspace too small for the split";
+        case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
+        case GEMM_ERR_DEVICE: return "GEMM_ERR_DEVICE: no usable gfx950 device";
+        default: return "unknown gemm_status_t";
+    }
+}
+
+gemm_status_t gemm_init(void) {
+    DeviceInfo dev;
+    return current_device(&dev);
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Device-side helpers shared by the gfx950 kernels: storage types, vector
+// bit casts, output rounding and the fused epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dge {
+
+// Input element types (match gemm_in_t) and output types (match gemm_out_t).
+enum : int { IN_F16 = 0, IN_BF16 = 1, IN_F32 = 2 };
+enum : int { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
+enum : int { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU = 2 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct InType;
+template <> struct InType<IN_F16> {
+    static constexpr int BYTES = 2;
+    __device__ static inline float to_f32(uint32_t bits) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    }
+};
+template <> struct InType<IN_BF16> {
+    static constexpr int BYTES = 2;
+    __device__ static inline float to_f32(uint32_t bits) {
+        return __builtin_bit_cast(float, bits << 16);  // bf16 is the top half of fp32
+    }
+};
+template <> struct InType<IN_F32> {
+    static constexpr int BYTES = 4;
+    __device__ static inline float to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits); }
+};
+
+// Load one element of an input array as raw bits (zero-extended).
+template <int DT>
+__device__ inline uint32_t load_elem_bits(const void* base, int64_t idx) {
+    if constexpr (InType<DT>::BYTES == 2)
+        return ((const uint16_t*)base)[idx];
+    else
+        return ((const uint32_t*)base)[idx];
+}
+
+template <int DT>
+__device__ inline float load_elem(const void* base, int64_t idx) {
+    return InType<DT>::to_f32(load_elem_bits<DT>(base, idx));
+}
+
+// Output element type: size and one round-to-nearest-even conversion.
+template <int OT> struct OutType;
+template <> struct OutType<OUT_F32> {
+    static constexpr int BYTES = 4;
+    typedef float T;
+    __device__ static inline float from_f32(float x) { return x; }
+    __device__ static inline float to_f32(float x) { return x; }
+};
+template <> struct OutType<OUT_F16> {
+    static constexpr int BYTES = 2;
+    typedef _Float16 T;
+    __device__ static inline _Float16 from_f32(float x) { return (_Float16)x; }
+    __device__ static inline float to_f32(_Float16 x) { return (float)x; }
+};
+template <> struct OutType<OUT_BF16> {
+    static constexpr int BYTES = 2;
+    typedef __bf16 T;
+    __device__ static inline __bf16 from_f32(float x) { return (__bf16)x; }
+    __device__ static inline float to_f32(__bf16 x) { return (float)x; }
+};
+
+// tanh form of GELU: 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))), in fp32.
+// tanh(u) = 1 - 2 / (1 + e^{2u}), evaluated with the device exp; the result
+// saturates correctly (e^{2u} -> inf gives 1, -> 0 gives -1).  The hardware
+// reciprocal (about 1 ulp) is ample for a value that is rounded to 16 bits.
+__device__ inline float gelu_tanh(float t) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    float u = c * (t + 0.044715f * t * t * t);
+    float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * u));
+    return 0.5f * t * (1.0f + th);
+}
+
+// Epilogue parameters, passed by value to every kernel that ends in C.
+struct Epilogue {
+    float alpha, beta;
+    int epi;           // EPI_*
+    const void* bias;  // N values of the input type, or null
+};
+
+// The fused epilogue on one accumulator value: alpha*acc + beta*old, + bias,
+// then GELU.  `old` is only meaningful when beta != 0.
+template <int DT>
+__device__ inline float apply_epilogue(const Epilogue& e, float acc, float old, int col) {
+    float t = e.alpha * acc;
+    if (e.beta != 0.0f) t += e.beta * old;
+    if (e.epi != EPI_NONE) t += load_elem<DT>(e.bias, col);
+    if (e.epi == EPI_BIAS_GELU) t = gelu_tanh(t);
+    return t;
+}
+
+// Map a linear workgroup id to a tile so that the workgroups dispatched to
+// one XCD (ids congruent mod 8 go to the same XCD) cover a compact block of
+// output tiles, ordered in groups of `group_m` tile rows: tiles that share
+// an A row panel or a B column panel then meet in the same 4 MB L2.
+__device__ inline int remap_xcd(int pid, int nwg) {
+    constexpr int NXCD = 8;
+    int per = (nwg + NXCD - 1) / NXCD;
+    int tall = nwg % NXCD;
+    if (tall == 0) tall = NXCD;
+    int xcd = pid % NXCD, local = pid / NXCD;
+    if (xcd < tall) return xcd * per + local;
+    return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+__device__ inline void grouped_tile(int lin, int tiles_m, int tiles_n, int group_m, int& tm,
+                                    int& tn) {
+    int in_group = group_m * tiles_n;
+    int g = lin / in_group;
+    int first_m = g * group_m;
+    int gsize = tiles_m - first_m;
+    if (gsize > group_m) gsize = group_m;
+    int r = lin % in_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+}  // namespace dge

@@ -1,0 +1,68 @@
+// Launchers for the vector-ALU ladder kernels, the split-K fixup and the q4
+// dequant.
+#include "dequant.h"
+#include "launch.h"
+
+namespace dge {
+
+template <int DT>
+static hipError_t naive_dt(const SimpleArgs& a, hipStream_t s) {
+    dim3 block(64, 4);
+    dim3 grid((a.N + 63) / 64, (a.M + 3) / 4);
+    hipLaunchKernelGGL((gemm_naive_kernel<DT>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s) {
+    switch (dt) {
+        case IN_F16: return naive_dt<IN_F16>(a, s);
+        case IN_BF16: return naive_dt<IN_BF16>(a, s);
+        default: return naive_dt<IN_F32>(a, s);
+    }
+}
+
+template <int DT>
+static hipError_t tiled_dt(const SimpleArgs& a, hipStream_t s) {
+    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+    hipLaunchKernelGGL((gemm_lds_tiled_kernel<DT>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s) {
+    switch (dt) {
+        case IN_F16: return tiled_dt<IN_F16>(a, s);
+        case IN_BF16: return tiled_dt<IN_BF16>(a, s);
+        default: return tiled_dt<IN_F32>(a, s);
+    }
+}
+
+template <int DT>
+static hipError_t fixup_dt(const SimpleArgs& a, const float* ws, int splits, hipStream_t s) {
+    const int64_t total = (int64_t)a.M * a.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((splitk_fixup_kernel<DT>), dim3((unsigned)blocks), dim3(256), 0, s, a, ws,
+                       splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_fixup(int dt, const SimpleArgs& a, const float* ws, int splits,
+                               hipStream_t s) {
+    switch (dt) {
+        case IN_F16: return fixup_dt<IN_F16>(a, ws, splits, s);
+        case IN_BF16: return fixup_dt<IN_BF16>(a, ws, splits, s);
+        default: return fixup_dt<IN_F32>(a, ws, splits, s);
+    }
+}
+
+hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
+                             int vec_out, hipStream_t s) {
+    const int64_t total = rows * (cols / 8);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 1 << 20) blocks = 1 << 20;
+    hipLaunchKernelGGL(dequant_q4_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, vec_out);
+    return hipGetLastError();
+}
+
+}  // namespace dge

@@ -1,0 +1,48 @@
+// Host-side launchers for the gfx950 kernels (C++ linkage; the C ABI in
+// api.cpp validates arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "ladder.h"
+#include "mfma_gemm.h"
+
+namespace dge {
+
+// Tile configurations (values match gemm_tile_t).
+enum : int { TILE_256x256 = 1, TILE_256x128 = 2, TILE_128x128 = 3, TILE_128x64 = 4 };
+
+struct TileShape {
+    int bm, bn;
+};
+inline TileShape tile_shape(int tile) {
+    switch (tile) {
+        case TILE_256x256: return {256, 256};
+        case TILE_256x128: return {256, 128};
+        case TILE_128x128: return {128, 128};
+        default: return {128, 64};
+    }
+}
+
+// Stage depth in elements: 128 bytes of K.
+inline int stage_k(int dt) { return dt == IN_F32 ? 32 : 64; }
+
+// Per-dtype MFMA launchers (one translation unit each).  `fast` selects the
+// unchecked load path (every tile full, K a multiple of the stage depth,
+// everything 16-byte aligned).
+hipError_t launch_mfma_f16(int tile, int trans_b, int fast, const MfmaArgs& a, int nwg,
+                           hipStream_t s);
+hipError_t launch_mfma_bf16(int tile, int trans_b, int fast, const MfmaArgs& a, int nwg,
+                            hipStream_t s);
+hipError_t launch_mfma_f32(int tile, int trans_b, int fast, const MfmaArgs& a, int nwg,
+                           hipStream_t s);
+
+hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s);
+hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s);
+hipError_t launch_splitk_fixup(int dt, const SimpleArgs& a, const float* ws, int splits,
+                               hipStream_t s);
+hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
+                             int vec_out, hipStream_t s);
+
+}  // namespace dge

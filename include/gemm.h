@@ -1,0 +1,176 @@
+/*
+ * gemm.h — C ABI of the MI355X (gfx950) dense-GEMM library.
+ *
+ * Operations
+ *   gemm_f16 / gemm_bf16 / gemm_f32:
+ *       C = epi(alpha * A * B + beta * C)
+ *     The dense product C_ij = sum_k A_ik B_kj, 2MNK FLOPs ("Matrix
+ *     Multiplication: The Operation Behind Modern AI", section "The operation
+ *     everything is made of"), accumulated in fp32 on the matrix cores
+ *     ("Optimizing GEMMs using tcgen05 - Part 2": fp16 in, fp32 accumulate).
+ *     epi adds one value per output column and optionally applies the tanh
+ *     form of GELU, 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))).
+ *   dequant_q4_f16:
+ *     expands 4-bit weight blocks into binary16 ("02 · 8m/8m② — Tiled wmma
+ *     f16 prefill GEMM", §2.3 and the q4_0 dequant kernel in §3.2).
+ *   prefill_q4_f16:
+ *     the prefill projection of the same page: dequantise an N x K q4 weight
+ *     into a caller-supplied binary16 scratch, then C = A * W^T on the same
+ *     stream (§1 route 2, §3.2 host routing).
+ *
+ * Conventions (all entry points)
+ *   - Row-major throughout; leading dimensions are in elements.
+ *       A: M x K, lda >= K.
+ *       B: K x N with ldb >= N (trans_b = 0), or N x K with ldb >= K
+ *          (trans_b = 1, the weight layout of the prefill page).
+ *       C: M x N, ldc >= N.
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains memory, and never
+ *     synchronises the host.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream); all work is enqueued on it.
+ *   - Arguments are validated on the host before any device call; a
+ *     rejected call enqueues nothing and returns a non-zero status.  No entry
+ *     point calls exit() or prints.
+ *   - M == 0 or N == 0 is a successful no-op.  K == 0 gives
+ *     C = epi(beta * C) (the product of empty sums is zero).
+ *   - beta == 0: C is write-only (its old contents, NaN included, are never
+ *     read).
+ *   - epi != GEMM_EPI_NONE requires bias != NULL: N values of the input type
+ *     (fp16 for gemm_f16, bf16 for gemm_bf16, fp32 for gemm_f32).
+ *   - C must not overlap A, B or bias (GEMM_ERR_INVALID_VALUE).
+ *   - Output rounding: one round-to-nearest-even from fp32 to c_type;
+ *     overflow gives +-inf; subnormals are kept.
+ *   - Unaligned pointers or leading dimensions that are not a multiple of
+ *     16 bytes take a slower element-wise load path; they are not errors.
+ *   - workspace: caller-owned device scratch for split-K partial sums.  If
+ *     it is NULL or smaller than gemm_workspace_size(), the call runs
+ *     without splitting K (it does not fail).
+ *   - Split-K partial sums are reduced in fixed order (split 0, 1, ...), so
+ *     results are bitwise reproducible run to run.
+ *   - Thread safety: calls may be issued concurrently from several host
+ *     threads (distinct streams or not); the only shared state is a
+ *     once-initialised device-property cache.
+ *
+ * Fault injection (tests): the environment variable GEMM_TEST_FAIL makes
+ * every entry point return a chosen error after validation and before any
+ * launch: "launch" -> GEMM_ERR_LAUNCH, "device" -> GEMM_ERR_DEVICE,
+ * "workspace" -> GEMM_ERR_WORKSPACE.  Nothing is enqueued in that case.
+ */
+#ifndef DGE_GEMM_H
+#define DGE_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer, enum or overlap */
+    GEMM_ERR_NOT_SUPPORTED = 2, /* valid request this build does not implement */
+    GEMM_ERR_WORKSPACE = 3,     /* explicit split request without enough workspace */
+    GEMM_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
+    GEMM_ERR_DEVICE = 5         /* no usable gfx950 device is current */
+} gemm_status_t;
+
+typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_BIAS = 1, GEMM_EPI_BIAS_GELU = 2 } gemm_epilogue_t;
+
+typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_F16 = 1, GEMM_OUT_BF16 = 2 } gemm_out_t;
+
+typedef enum { GEMM_IN_F16 = 0, GEMM_IN_BF16 = 1, GEMM_IN_F32 = 2 } gemm_in_t;
+
+/* Kernel families, for gemm_ex's explicit selection. */
+typedef enum {
+    GEMM_ALGO_AUTO = 0,      /* library's choice by shape */
+    GEMM_ALGO_NAIVE = 1,     /* one thread per output element, no reuse (the floor) */
+    GEMM_ALGO_LDS_TILED = 2, /* LDS tiles + register-blocked fp32 FMA, no matrix cores */
+    GEMM_ALGO_MFMA = 3       /* LDS-staged macro tiles on the matrix cores */
+} gemm_algo_t;
+
+/* Tile configurations of the MFMA family (macro tile BM x BN, waves). */
+typedef enum {
+    GEMM_TILE_AUTO = 0,
+    GEMM_TILE_256x256 = 1, /* 4 waves, 128 x 128 per wave */
+    GEMM_TILE_256x128 = 2, /* 4 waves, 128 x 64 per wave */
+    GEMM_TILE_128x128 = 3, /* 4 waves, 64 x 64 per wave */
+    GEMM_TILE_128x64 = 4   /* 4 waves, 64 x 32 per wave */
+} gemm_tile_t;
+
+typedef struct {
+    int algo;   /* gemm_algo_t */
+    int tile;   /* gemm_tile_t; MFMA family only */
+    int splits; /* 0 = auto, 1 = never split, s > 1 = split K into s slices
+                   (needs gemm_workspace_size_splits(M, N, s) bytes) */
+} gemm_tuning_t;
+
+/* fp16 A/B/bias, fp32 accumulate, c_type output. */
+gemm_status_t gemm_f16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+                       gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* bf16 A/B/bias, fp32 accumulate, c_type output. */
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+                        gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* fp32 A/B/bias, fp32 accumulate (fp32 matrix-core path by default);
+ * c_type must be GEMM_OUT_F32. */
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, int trans_b, float beta, void* C, int64_t ldc,
+                       gemm_out_t c_type, gemm_epilogue_t epi, const void* bias, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* The same operation with the input type and the kernel family, tile and
+ * split chosen explicitly (tuning may be NULL = all automatic).  Used by the
+ * fp32 ladder (naive -> LDS-tiled -> MFMA) and by tile and split sweeps.  A
+ * split request (splits > 1) with too little workspace returns
+ * GEMM_ERR_WORKSPACE; the naive and LDS-tiled families never split. */
+gemm_status_t gemm_ex(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float alpha,
+                      const void* A, int64_t lda, const void* B, int64_t ldb, int trans_b,
+                      float beta, void* C, int64_t ldc, gemm_out_t c_type, gemm_epilogue_t epi,
+                      const void* bias, void* workspace, size_t workspace_bytes,
+                      const gemm_tuning_t* tuning, void* stream);
+
+/* q4 -> binary16.  q holds rows * (cols/32) blocks of 18 bytes, row-major
+ * (block (r, b) at byte 18 * (r * cols/32 + b)): a little-endian binary16
+ * scale d, then 16 bytes whose low nibble is element i and high nibble
+ * element i + 16 of the block.  out[r * ldo + 32 b + e] = RNE16(d * (code - 8)).
+ * Requires cols % 32 == 0, ldo >= cols, q 2-byte aligned and out 2-byte
+ * aligned (GEMM_ERR_INVALID_VALUE otherwise).  The result is bit-exact
+ * (the product is exact in fp32). */
+gemm_status_t dequant_q4_f16(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
+                             void* stream);
+
+/* Prefill projection: w16 (caller scratch, N x K binary16, >= 2*N*K bytes)
+ * = dequant(q); then C = epi(A * w16^T), A M x K fp16 (lda), C M x N (ldc,
+ * c_type), alpha = 1, beta = 0.  K % 32 == 0 is required.  Both steps are
+ * enqueued on `stream`; w16 holds the dequantised weight afterwards. */
+gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* q, void* w16, void* C, int64_t ldc, gemm_out_t c_type,
+                             gemm_epilogue_t epi, const void* bias, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace bytes the automatic schedule of this shape would use (0 if it
+ * would not split K).  dtype is a gemm_in_t. */
+size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype);
+
+/* Workspace bytes an explicit split into `splits` slices needs. */
+size_t gemm_workspace_size_splits(int64_t M, int64_t N, int splits);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gemm_status_string(gemm_status_t s);
+
+/* Checks that the current device is a gfx950 and caches its properties.
+ * Called implicitly by every compute entry point; may be called first to
+ * pay the one-time cost outside a timed region. */
+gemm_status_t gemm_init(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGE_GEMM_H */

@@ -7,10 +7,26 @@ Random-input floating-point results pass when both hold:
     with U_ij = sum_k |A_ik||B_kj| from the oracle.
 Integer-valued runs and the q4 dequant must match the oracle's rounded bits
 exactly.  T is the oracle's binary64 result before output rounding.
+
+bfloat16 OUTPUT: one rounding to bfloat16 alone has a relative error of up to
+2^-9 per element (RMS about 2^-9/sqrt(3) = 1.1e-3 for uniformly spread
+significands), which exceeds the 1e-3 normwise bound by construction.  For
+that output type the normwise bound is widened by the bfloat16 unit
+roundoff u = 2^-8 (1e-3 + 2^-8); the elementwise bound is unchanged (the
+rounding, at most 2^-9 |T| <= 2^-9 scale, fits inside 1e-2 * scale).
+Inputs in bfloat16 with fp16 or fp32 output keep the 1e-3 bound.
 """
 import numpy as np
 
 NORMWISE_TOL = 1e-3
+BF16_OUT_NORMWISE_TOL = 1e-3 + 2.0 ** -8
+
+
+def normwise_tol(out_type):
+    """Normwise bound for an output type name ('f16', 'bf16', 'f32')."""
+    return BF16_OUT_NORMWISE_TOL if out_type == "bf16" else NORMWISE_TOL
+
+
 ELEM_RTOL = 1e-2
 ELEM_ATOL = 1e-3
 

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/gemm.h declares, and rejects invalid arguments on the
+host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dense_gemm_engineering_amd.binding as dge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "gemm.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+([a-z_0-9]+)\s*\(", src,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(dge.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    L = dge.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for s in range(6):
+        assert dge.gemm_status_string(s).startswith(dge.STATUS_NAMES[s])
+    assert "unknown" in dge.gemm_status_string(99)
+
+
+def _call(L, **kw):
+    a = dict(M=4, N=4, K=4, alpha=1.0, A=8, lda=4, B=4096, ldb=4, trans_b=0, beta=0.0, C=65536,
+             ldc=4, c_type=1, epi=0, bias=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.gemm_f16(a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"], a["B"], a["ldb"],
+                      a["trans_b"], a["beta"], a["C"], a["ldc"], a["c_type"], a["epi"], a["bias"],
+                      a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [dict(M=-1), dict(K=-2), dict(lda=3), dict(ldb=3), dict(ldc=3),
+                                 dict(trans_b=2), dict(c_type=7), dict(epi=3),
+                                 dict(epi=1, bias=None), dict(C=None), dict(A=None),
+                                 dict(alpha=float("nan")), dict(C=8),  # C overlaps A
+                                 dict(trans_b=1, ldb=3), dict(M=1 << 31)])
+def test_invalid_arguments_rejected_on_host(bad):
+    assert _call(dge.lib(), **bad) == 1
+
+
+def test_empty_problem_is_ok_without_device():
+    assert _call(dge.lib(), M=0) == 0
+    assert _call(dge.lib(), N=0, C=None) in (0, 1)
+
+
+def test_fp32_requires_fp32_output():
+    L = dge.lib()
+    st = L.gemm_f32(4, 4, 4, 1.0, 8, 4, 4096, 4, 0, 0.0, 65536, 4, 1, 0, None, None, 0, None)
+    assert st == 1
+
+
+def test_dequant_validation():
+    L = dge.lib()
+    assert L.dequant_q4_f16(2, 4096, 4, 16, 16, None) == 1   # cols not a multiple of 32
+    assert L.dequant_q4_f16(3, 4096, 4, 32, 32, None) == 1   # odd q address
+    assert L.dequant_q4_f16(2, 4096, 4, 32, 31, None) == 1   # ldo < cols
+    assert L.dequant_q4_f16(2, 4096, 0, 32, 32, None) == 0   # empty
+
+
+def test_prefill_validation():
+    L = dge.lib()
+    # K not a multiple of 32
+    assert L.prefill_q4_f16(4, 4, 40, 8, 40, 4096, 1 << 20, 1 << 24, 4, 1, 0, None, None, 0,
+                            None) == 1
+
+
+def test_workspace_sizes():
+    assert dge.gemm_workspace_size_splits(100, 50, 1) == 0
+    assert dge.gemm_workspace_size_splits(100, 50, 3) == 3 * 100 * 50 * 4
+    assert dge.gemm_workspace_size(0, 5, 5) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
+def test_no_device_reports_device_error():
+    assert dge.lib().gemm_init() == 5
+    assert _call(dge.lib()) == 5
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
+def test_forced_failure_hook(monkeypatch):
+    monkeypatch.setenv("GEMM_TEST_FAIL", "launch")
+    assert _call(dge.lib()) == 4
+    monkeypatch.setenv("GEMM_TEST_FAIL", "workspace")
+    assert _call(dge.lib()) == 3
+    monkeypatch.setenv("GEMM_TEST_FAIL", "launch")
+    assert _call(dge.lib(), M=-1) == 1  # validation first

@@ -1,0 +1,251 @@
+"""GPU parity of the GEMM entry points against the oracle, at sizes the
+oracle finishes in seconds: several tiles, ragged tails, every epilogue,
+output type, kernel family, tile and split, misaligned operands, K = 0.
+
+Random inputs are judged by the normwise and elementwise bounds; integer
+inputs (every partial sum exactly representable in fp32) must match the
+oracle's rounded result bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dense_gemm_engineering_amd.binding as dge
+from dense_gemm_engineering_amd import inputs
+from gpu_util import assert_bits, assert_close, to_dev, bits_of
+
+pytestmark = pytest.mark.gpu
+
+TILES = ["256x256", "256x128", "128x128", "128x64"]
+
+
+def _operands(M, N, K, dtype, trans_b, integer, seed):
+    r = np.random.Generator(np.random.PCG64(seed))
+    if integer:
+        a = r.integers(-4, 5, (M, K)).astype(np.float64)
+        b = r.integers(-4, 5, (K, N)).astype(np.float64)
+    else:
+        a = r.uniform(-1, 1, (M, K))
+        b = r.uniform(-1, 1, (K, N))
+    A = inputs.to_bits(a, dtype)
+    Bkn = inputs.to_bits(b, dtype)
+    B = np.ascontiguousarray(Bkn.T) if trans_b else Bkn
+    return A, B
+
+
+def _run(A, B, dtype, trans_b, out, **kw):
+    dA, dB = to_dev(A, dtype), to_dev(B, dtype)
+    C = dge.gemm_ex(dA, dB, trans_b=trans_b, out_dtype=out, **kw)
+    torch.cuda.synchronize()
+    return C
+
+
+def test_cfg1_uniform_fp32_out_every_family():
+    A, B = inputs.cfg1()
+    T, U = oracle.gemm(A, B, "f16")
+    for algo, tile in [("naive", "auto"), ("lds_tiled", "auto")] + [("mfma", t) for t in TILES]:
+        C = _run(A, B, "f16", False, torch.float32, algo=algo, tile=tile)
+        assert_close(C, T, U, what="%s/%s" % (algo, tile))
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.float16])
+def test_cfg1_integer_bit_exact_every_family(out):
+    A, B = inputs.cfg1(integer=True)
+    T, _ = oracle.gemm(A, B, "f16")
+    for algo, tile in [("naive", "auto"), ("lds_tiled", "auto")] + [("mfma", t) for t in TILES]:
+        C = _run(A, B, "f16", False, out, algo=algo, tile=tile)
+        assert_bits(C, T, what="%s/%s" % (algo, tile))
+
+
+SHAPES = [(33, 70, 256), (1, 1, 1), (257, 129, 65), (100, 300, 160), (5, 520, 8), (300, 7, 1000),
+          (512, 512, 192), (130, 260, 96)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_ragged_shapes(M, N, K, trans_b, dtype):
+    A, B = _operands(M, N, K, dtype, trans_b, False, M * 7 + N * 3 + K)
+    T, U = oracle.gemm(A, B, dtype, trans_b=trans_b)
+    for tile in TILES:
+        C = _run(A, B, dtype, trans_b, torch.float16, algo="mfma", tile=tile)
+        assert_close(C, T, U, what="%s %s" % (dtype, tile))
+    Ai, Bi = _operands(M, N, K, dtype, trans_b, True, M + N + K)
+    Ti, _ = oracle.gemm(Ai, Bi, dtype, trans_b=trans_b)
+    for tile in TILES:
+        C = _run(Ai, Bi, dtype, trans_b, torch.float32, algo="mfma", tile=tile)
+        assert_bits(C, Ti, what="int %s %s" % (dtype, tile))
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("M,N,K", [(96, 200, 300), (256, 256, 512), (33, 70, 256)])
+def test_fp32_inputs_every_family(M, N, K, trans_b):
+    A, B = _operands(M, N, K, "f32", trans_b, False, 11 + M)
+    T, U = oracle.gemm(A, B, "f32", trans_b=trans_b)
+    for algo, tile in [("naive", "auto"), ("lds_tiled", "auto")] + [("mfma", t) for t in TILES]:
+        C = _run(A, B, "f32", trans_b, torch.float32, algo=algo, tile=tile)
+        assert_close(C, T, U, what="%s/%s" % (algo, tile))
+    Ai, Bi = _operands(M, N, K, "f32", trans_b, True, 12 + M)
+    Ti, _ = oracle.gemm(Ai, Bi, "f32", trans_b=trans_b)
+    for algo, tile in [("naive", "auto"), ("lds_tiled", "auto")] + [("mfma", t) for t in TILES]:
+        C = _run(Ai, Bi, "f32", trans_b, torch.float32, algo=algo, tile=tile)
+        assert_bits(C, Ti, what="int %s/%s" % (algo, tile))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("out", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu"])
+def test_epilogues_alpha_beta(epi, out, dtype):
+    M, N, K = 160, 200, 96
+    A, B = _operands(M, N, K, dtype, False, False, 77)
+    r = np.random.Generator(np.random.PCG64(78))
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), dtype)
+    out_name = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[out]
+    cold_bits = inputs.to_bits(r.uniform(-1, 1, (M, N)), out_name)
+    cold = oracle.decode(cold_bits, out_name)
+    bias = oracle.decode(bias_bits, dtype)
+    alpha, beta = 0.75, -0.5
+    T, U = oracle.gemm(A, B, dtype, alpha=alpha, beta=beta, C_old=cold, epi=epi, bias=bias)
+    for tile in ["256x256", "128x64"]:
+        C = to_dev(cold_bits, out_name)
+        dge.gemm_ex(to_dev(A, dtype), to_dev(B, dtype), C, alpha=alpha, beta=beta, epi=epi,
+                    bias=to_dev(bias_bits, dtype) if epi != "none" else None, algo="mfma",
+                    tile=tile)
+        torch.cuda.synchronize()
+        assert_close(C, T, U, alpha, beta, cold, bias if epi != "none" else None,
+                     what="%s %s" % (epi, tile))
+
+
+def test_integer_bias_bit_exact_and_beta_zero_ignores_nan():
+    M, N, K = 200, 136, 128
+    A, B = _operands(M, N, K, "f16", True, True, 90)
+    r = np.random.Generator(np.random.PCG64(91))
+    bias_bits = inputs.to_bits(r.integers(-20, 21, N).astype(float), "f16")
+    T, _ = oracle.gemm(A, B, "f16", trans_b=True, epi="bias", bias=oracle.decode(bias_bits, "f16"))
+    for tile in TILES:
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        dge.gemm_ex(to_dev(A, "f16"), to_dev(B, "f16"), C, trans_b=True, epi="bias",
+                    bias=to_dev(bias_bits, "f16"), algo="mfma", tile=tile)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what=tile)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5])
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_split_k_exact_and_deterministic(splits, trans_b):
+    M, N, K = 256, 384, 1024 + 64
+    A, B = _operands(M, N, K, "f16", trans_b, True, 100 + splits)
+    T, _ = oracle.gemm(A, B, "f16", trans_b=trans_b)
+    ws = torch.empty(dge.gemm_workspace_size_splits(M, N, splits) // 4 + 1, dtype=torch.float32,
+                     device="cuda")
+    dA, dB = to_dev(A, "f16"), to_dev(B, "f16")
+    for tile in ["256x256", "128x128"]:
+        C = dge.gemm_ex(dA, dB, trans_b=trans_b, out_dtype=torch.float32, workspace=ws,
+                        algo="mfma", tile=tile, splits=splits)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what="splits=%d %s" % (splits, tile))
+    Af, Bf = _operands(M, N, K, "f16", trans_b, False, 200 + splits)
+    Tf, Uf = oracle.gemm(Af, Bf, "f16", trans_b=trans_b)
+    dA, dB = to_dev(Af, "f16"), to_dev(Bf, "f16")
+    runs = []
+    for _ in range(2):
+        C = dge.gemm_ex(dA, dB, trans_b=trans_b, out_dtype=torch.float16, workspace=ws,
+                        algo="mfma", tile="256x256", splits=splits, epi="bias_gelu",
+                        bias=torch.zeros(N, dtype=torch.float16, device="cuda"))
+        torch.cuda.synchronize()
+        runs.append(bits_of(C))
+    assert np.array_equal(runs[0], runs[1])
+    Tg, Ug = oracle.gemm(Af, Bf, "f16", trans_b=trans_b, epi="bias_gelu", bias=np.zeros(N))
+    assert_close(C, Tg, Ug, what="split gelu")
+
+
+def test_split_request_without_workspace_is_an_error():
+    A, B = _operands(64, 64, 512, "f16", False, False, 5)
+    with pytest.raises(dge.GemmError) as e:
+        _run(A, B, "f16", False, torch.float16, algo="mfma", splits=2)
+    assert e.value.status == 3
+
+
+def test_k_zero_is_beta_c_plus_bias():
+    M, N = 70, 90
+    r = np.random.Generator(np.random.PCG64(300))
+    cold_bits = inputs.to_bits(r.uniform(-1, 1, (M, N)), "f32")
+    bias_bits = inputs.to_bits(r.uniform(-1, 1, N), "f16")
+    C = to_dev(cold_bits, "f32")
+    A = torch.empty((M, 0), dtype=torch.float16, device="cuda")
+    B = torch.empty((0, N), dtype=torch.float16, device="cuda")
+    dge.gemm_f16(A, B, C, beta=2.0, epi="bias", bias=to_dev(bias_bits, "f16"))
+    torch.cuda.synchronize()
+    T, _ = oracle.gemm(np.zeros((M, 0), np.uint16), np.zeros((0, N), np.uint16), "f16", beta=2.0,
+                       C_old=oracle.decode(cold_bits, "f32"), epi="bias",
+                       bias=oracle.decode(bias_bits, "f16"))
+    assert_bits(C, T)
+
+
+def test_empty_m_or_n_is_a_no_op():
+    A = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    B = torch.ones((64, 32), dtype=torch.float16, device="cuda")
+    C = dge.gemm_f16(A, B)
+    assert C.shape == (0, 32)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_misaligned_pointers_and_odd_leading_dimensions(dtype):
+    # A starts one element into its buffer and has an odd leading dimension;
+    # C's leading dimension is odd too: the element-wise load/store path.
+    M, N, K = 130, 75, 203
+    lda, ldc = K + 3, N + 1
+    r = np.random.Generator(np.random.PCG64(400))
+    A, B = _operands(M, N, K, dtype, False, True, 401)
+    Abig = np.zeros((M, lda + 1), dtype=A.dtype)
+    Abig[:, 1:K + 1] = A
+    dAbig = to_dev(Abig.reshape(-1), dtype)
+    dA = dAbig[1:].as_strided((M, K), (lda + 1, 1))
+    T, _ = oracle.gemm(A, B, dtype)
+    out = torch.float32
+    Cbig = torch.zeros((M, ldc), dtype=out, device="cuda")
+    C = Cbig[:, :N]
+    for tile in ["256x256", "128x64"]:
+        dge.gemm_ex(dA, to_dev(B, dtype), C, algo="mfma", tile=tile)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what=tile)
+    del r
+
+
+def test_identity_and_permutation_on_gpu():
+    M, K = 192, 256
+    A = inputs.uniform((M, K), "f16", 95, 1)
+    perm = np.random.Generator(np.random.PCG64(96)).permutation(K)
+    P = np.zeros((K, K))
+    P[perm, np.arange(K)] = 1.0
+    for trans_b in (False, True):
+        Pb = inputs.to_bits(P, "f16")
+        B = np.ascontiguousarray(Pb.T) if trans_b else Pb
+        for tile in TILES:
+            C = _run(A, B, "f16", trans_b, torch.float16, algo="mfma", tile=tile)
+            assert np.array_equal(bits_of(C), A[:, perm]), tile
+
+
+def test_invalid_arguments_rejected():
+    A = torch.ones((8, 8), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        dge.gemm_f16(A, torch.ones((9, 8), dtype=torch.float16, device="cuda"))
+    with pytest.raises(dge.GemmError) as e:
+        dge.gemm_f16(A, A, epi="bias", bias=None)
+    assert e.value.status == 1
+    with pytest.raises(dge.GemmError) as e:  # C aliases A
+        dge.gemm_f16(A, A, A)
+    assert e.value.status == 1
+
+
+def test_forced_launch_failure(monkeypatch):
+    A = torch.ones((8, 8), dtype=torch.float16, device="cuda")
+    monkeypatch.setenv("GEMM_TEST_FAIL", "launch")
+    with pytest.raises(dge.GemmError) as e:
+        dge.gemm_f16(A, A)
+    assert e.value.status == 4
+    monkeypatch.setenv("GEMM_TEST_FAIL", "")
+    C = dge.gemm_f16(A, A, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(C == 8)

@@ -160,3 +160,16 @@ def test_k_zero_gives_beta_c():
     C = np.arange(12, dtype=np.float64).reshape(3, 4)
     T, U = oracle.gemm(A, B, "f16", beta=2.0, C_old=C)
     assert np.array_equal(T, 2 * C) and np.all(U == 0)
+
+
+def test_bf16_output_rounding_exceeds_1e3_by_construction():
+    # Why bf16 outputs get the widened normwise bound: rounding an exact
+    # result to bf16 alone already gives ~1.1e-3 normwise relative error.
+    from oracle import compare
+    A, B = inputs.cfg1()
+    T, _ = oracle.gemm(A[:64], B, "f16")
+    Cb = oracle.decode(oracle.encode(T, "bf16"), "bf16")
+    e = compare.normwise_rel_err(Cb, T)
+    assert 1e-3 < e < compare.normwise_tol("bf16")
+    Ch = oracle.decode(oracle.encode(T, "f16"), "f16")
+    assert compare.normwise_rel_err(Ch, T) < 1e-3 / 2
