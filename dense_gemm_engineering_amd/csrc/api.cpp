@@ -161,29 +161,35 @@ int env_int(const char* name, int dflt) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Relative MFMA throughput of each tile when the chip is full (the bigger
-// the per-wave tile, the more MFMAs each LDS byte feeds), and how many of
-// its workgroups one CU holds.
+// Per-CU MFMA throughput of each tile configuration with the chip full,
+// relative to the 8-wave 256 x 256 tile (measured on MI355X at 4096^3, fp16,
+// direct-to-LDS path): one wave per SIMD cannot keep the MFMA pipe busy,
+// so the 4-wave 256-wide tiles lag; 128 x 128 runs two workgroups per CU.
 double tile_efficiency(int tile) {
     switch (tile) {
-        case TILE_256x256: return 1.0;
-        case TILE_256x128: return 0.9;
-        case TILE_128x128: return 0.75;
-        default: return 0.55;
+        case TILE_256x256_W8: return 1.0;
+        case TILE_256x256: return 0.7;
+        case TILE_256x128: return 0.55;
+        case TILE_128x128: return 0.72;
+        default: return 0.5;
     }
 }
-int tile_occupancy(int tile) { return tile == TILE_256x256 || tile == TILE_256x128 ? 1 : 2; }
+int tile_occupancy(int tile) {
+    return tile == TILE_256x256 || tile == TILE_256x128 || tile == TILE_256x256_W8 ? 1 : 2;
+}
 
-// Pick the tile that minimises (rounds of workgroups) x (tile work) / efficiency.
+// Pick the tile that minimises rounds x (work of the tiles a CU runs per
+// round) / efficiency.
 int choose_tile(int64_t M, int64_t N, int cus) {
-    int best = TILE_256x256;
+    int best = TILE_256x256_W8;
     double best_cost = 1e300;
-    for (int t = TILE_256x256; t <= TILE_128x64; ++t) {
+    for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
         const TileShape ts = tile_shape(t);
         const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
         const int64_t slots = (int64_t)cus * tile_occupancy(t);
         const int64_t rounds = (tiles + slots - 1) / slots;
-        const double cost = (double)rounds * ts.bm * ts.bn / tile_efficiency(t);
+        const double cost =
+            (double)rounds * tile_occupancy(t) * ts.bm * ts.bn / tile_efficiency(t);
         if (cost < best_cost * 0.999) {
             best_cost = cost;
             best = t;
@@ -214,9 +220,11 @@ gemm_status_t launch_status(hipError_t e) {
     return GEMM_ERR_LAUNCH;
 }
 
-gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus) {
+// direct: 0 = register-staged kernel only, 1 = direct-to-LDS kernel when the
+// problem qualifies (full tiles, 16-bit inputs, aligned operands).
+gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct) {
     if (tile == GEMM_TILE_AUTO) tile = choose_tile(g.M, g.N, cus);
-    if (tile < TILE_256x256 || tile > TILE_128x64) return GEMM_ERR_INVALID_VALUE;
+    if (tile < TILE_256x256 || tile > TILE_LAST) return GEMM_ERR_INVALID_VALUE;
     const TileShape ts = tile_shape(tile);
     const int bk = stage_k(g.dt);
     const int max_splits = std::max(1, ceil_div(g.K, bk));
@@ -264,6 +272,16 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus) {
     const int64_t nwg = (int64_t)a.tiles_m * a.tiles_n * splits;
     if (nwg > 0x7fffffff) return GEMM_ERR_NOT_SUPPORTED;
     hipError_t e;
+    const bool use_direct = direct && fast && g.dt != IN_F32 &&
+                            (g.trans_b || ts.bn >= 128) && env_int("GEMM_DIRECT", 1) != 0;
+    if (use_direct) {
+        e = g.dt == IN_F16 ? launch_mfma_direct_f16(tile, g.trans_b, a, (int)nwg, g.stream)
+                           : launch_mfma_direct_bf16(tile, g.trans_b, a, (int)nwg, g.stream);
+        if (e != hipSuccess) return launch_status(e);
+        if (splits > 1)
+            e = launch_splitk_fixup(g.dt, simple_args(g), (const float*)g.ws, splits, g.stream);
+        return launch_status(e);
+    }
     switch (g.dt) {
         case IN_F16: e = launch_mfma_f16(tile, g.trans_b, fast, a, (int)nwg, g.stream); break;
         case IN_BF16: e = launch_mfma_bf16(tile, g.trans_b, fast, a, (int)nwg, g.stream); break;
@@ -279,8 +297,8 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
     if (st != GEMM_OK) return st;
     gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
     if (tuning) tn = *tuning;
-    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_MFMA) return GEMM_ERR_INVALID_VALUE;
-    if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_128x64) return GEMM_ERR_INVALID_VALUE;
+    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_MFMA_DIRECT) return GEMM_ERR_INVALID_VALUE;
+    if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8) return GEMM_ERR_INVALID_VALUE;
     if (tn.splits < 0) return GEMM_ERR_INVALID_VALUE;
     if (g.M == 0 || g.N == 0) return GEMM_OK;
     if ((st = forced_failure()) != GEMM_OK) return st;
@@ -293,8 +311,10 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
         case GEMM_ALGO_LDS_TILED:
             if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
             return launch_status(launch_lds_tiled(g.dt, simple_args(g), g.stream));
+        case GEMM_ALGO_MFMA:
+            return run_mfma(g, tn.tile, tn.splits, dev.cus, 0);
         default:
-            return run_mfma(g, tn.tile, tn.splits, dev.cus);
+            return run_mfma(g, tn.tile, tn.splits, dev.cus, 1);
     }
 }
 

@@ -11,7 +11,8 @@
 namespace dge {
 
 // Tile configurations (values match gemm_tile_t).
-enum : int { TILE_256x256 = 1, TILE_256x128 = 2, TILE_128x128 = 3, TILE_128x64 = 4 };
+enum : int { TILE_256x256 = 1, TILE_256x128 = 2, TILE_128x128 = 3, TILE_128x64 = 4,
+              TILE_256x256_W8 = 5, TILE_LAST = 5 };
 
 struct TileShape {
     int bm, bn;
@@ -21,6 +22,7 @@ inline TileShape tile_shape(int tile) {
         case TILE_256x256: return {256, 256};
         case TILE_256x128: return {256, 128};
         case TILE_128x128: return {128, 128};
+        case TILE_256x256_W8: return {256, 256};
         default: return {128, 64};
     }
 }
@@ -37,6 +39,12 @@ hipError_t launch_mfma_bf16(int tile, int trans_b, int fast, const MfmaArgs& a, 
                             hipStream_t s);
 hipError_t launch_mfma_f32(int tile, int trans_b, int fast, const MfmaArgs& a, int nwg,
                            hipStream_t s);
+
+// Direct-to-LDS variant (16-bit inputs, full tiles, 16-byte aligned operands).
+// Returns hipErrorInvalidValue for a tile it does not provide.
+hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, hipStream_t s);
+hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg,
+                                   hipStream_t s);
 
 hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s);
 hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s);

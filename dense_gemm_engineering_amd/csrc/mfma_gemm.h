@@ -290,6 +290,71 @@ __device__ inline void finish_row8(const MfmaArgs& p, int row, int col, const fl
     store_row8<OT>(p.C, p.ldc, row, col, p.N, t, vec);
 }
 
+// ---- a4: the fused epilogue of one workgroup tile.  Each wave stages its
+// accumulators through LDS 16 rows at a time (stg: NW x 16 x (WTN + 4) fp32)
+// and writes 8 consecutive columns per lane, so a wave stores whole rows;
+// with a split-K workspace the raw fp32 partials go there instead.
+template <int DT, int BM, int BN, int WM, int WN, int MODE, int TM, int TN>
+__device__ inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], float* stg_all,
+                                     int m0, int n0, int split) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
+    constexpr int PITCH = WTN + 4;  // floats; the pad staggers rows across banks
+    float* stg = stg_all + wave * (16 * PITCH);
+    constexpr int LPR = WTN / 8;  // lanes per row, 8 columns each
+    constexpr int RPP = 64 / LPR; // rows per pass
+    static_assert(LPR * 8 == WTN && RPP * LPR == 64 && 16 % RPP == 0, "epilogue lane map");
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                stg[(4 * (lane >> 4) + e) * PITCH + 16 * j + (lane & 15)] = acc[i][j][e];
+        __syncthreads();
+        // The read-back loop does not touch the accumulators; keeping it
+        // rolled keeps the strip loop small enough to unroll fully, so the
+        // accumulator array is only ever indexed statically (no scratch).
+#pragma nounroll
+        for (int pass = 0; pass < 16 / RPP; ++pass) {
+            const int r = pass * RPP + lane / LPR;
+            const int c8 = (lane % LPR) * 8;
+            const int grow = m0 + wm0 + 16 * i + r;
+            const int gcol = n0 + wn0 + c8;
+            float v[8];
+            const f32x4 lo = *(const f32x4*)&stg[r * PITCH + c8];
+            const f32x4 hi = *(const f32x4*)&stg[r * PITCH + c8 + 4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = lo[e];
+                v[4 + e] = hi[e];
+            }
+            if (MODE == LOAD_EDGE && (grow >= p.M || gcol >= p.N)) continue;
+            if (p.ws) {
+                float* w = p.ws + ((int64_t)split * p.M + grow) * p.N + gcol;
+                if (p.vec_ok && gcol + 8 <= p.N && (p.N & 3) == 0) {
+                    *(f32x4*)w = lo;
+                    *(f32x4*)(w + 4) = hi;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (gcol + e < p.N) w[e] = v[e];
+                }
+            } else if (p.c_type == OUT_F16) {
+                finish_row8<DT, OUT_F16>(p, grow, gcol, v);
+            } else if (p.c_type == OUT_BF16) {
+                finish_row8<DT, OUT_BF16>(p, grow, gcol, v);
+            } else {
+                finish_row8<DT, OUT_F32>(p, grow, gcol, v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MODE>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(MfmaArgs p) {
     constexpr int NT = WM * WN * 64;
@@ -374,6 +439,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(MfmaArgs p) 
     static_assert(CH == 8, "two 4-chunk k-blocks per stage");
     u32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 
+    static_assert(WM * WN * 16 * (WTN + 4) * 4 <= (int)sizeof(lds), "epilogue staging must fit");
+
     // ---- a2: prologue.  Stage 0 goes to LDS buffer 0; stage 1 waits in
     // registers.  In the steady state the registers always hold the stage
     // after the one being computed, so every global load has a whole stage
@@ -418,60 +485,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(MfmaArgs p) 
     }
     __syncthreads();
 
-    // ---- a4: epilogue through LDS, 16 rows of the wave tile at a time
-    constexpr int PITCH = WTN + 4;  // floats; the pad staggers rows across banks
-    static_assert(NT / 64 * 16 * PITCH * 4 <= (int)sizeof(lds), "epilogue staging must fit");
-    float* stg = (float*)&lds[0][0] + wave * (16 * PITCH);
-    constexpr int LPR = WTN / 8;  // lanes per row, 8 columns each
-    constexpr int RPP = 64 / LPR; // rows per pass
-    static_assert(LPR * 8 == WTN && RPP * LPR == 64 && 16 % RPP == 0, "epilogue lane map");
-
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                stg[(4 * (lane >> 4) + e) * PITCH + 16 * j + (lane & 15)] = acc[i][j][e];
-        __syncthreads();
-        // The read-back loop does not touch the accumulators; keeping it
-        // rolled keeps the strip loop small enough to unroll fully, so the
-        // accumulator array is only ever indexed statically (no scratch).
-#pragma nounroll
-        for (int pass = 0; pass < 16 / RPP; ++pass) {
-            const int r = pass * RPP + lane / LPR;
-            const int c8 = (lane % LPR) * 8;
-            const int grow = m0 + wm0 + 16 * i + r;
-            const int gcol = n0 + wn0 + c8;
-            float v[8];
-            const f32x4 lo = *(const f32x4*)&stg[r * PITCH + c8];
-            const f32x4 hi = *(const f32x4*)&stg[r * PITCH + c8 + 4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = lo[e];
-                v[4 + e] = hi[e];
-            }
-            if (MODE == LOAD_EDGE && (grow >= p.M || gcol >= p.N)) continue;
-            if (p.ws) {
-                float* w = p.ws + ((int64_t)split * p.M + grow) * p.N + gcol;
-                if (p.vec_ok && gcol + 8 <= p.N && (p.N & 3) == 0) {
-                    *(f32x4*)w = lo;
-                    *(f32x4*)(w + 4) = hi;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gcol + e < p.N) w[e] = v[e];
-                }
-            } else if (p.c_type == OUT_F16) {
-                finish_row8<DT, OUT_F16>(p, grow, gcol, v);
-            } else if (p.c_type == OUT_BF16) {
-                finish_row8<DT, OUT_BF16>(p, grow, gcol, v);
-            } else {
-                finish_row8<DT, OUT_F32>(p, grow, gcol, v);
-            }
-        }
-        __syncthreads();
-    }
+    epilogue_tile<DT, BM, BN, WM, WN, MODE>(p, acc, (float*)&lds[0][0], m0, n0, split);
 }
 
 }  // namespace dge

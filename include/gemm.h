@@ -86,7 +86,11 @@ typedef enum {
     GEMM_ALGO_AUTO = 0,      /* library's choice by shape */
     GEMM_ALGO_NAIVE = 1,     /* one thread per output element, no reuse (the floor) */
     GEMM_ALGO_LDS_TILED = 2, /* LDS tiles + register-blocked fp32 FMA, no matrix cores */
-    GEMM_ALGO_MFMA = 3       /* LDS-staged macro tiles on the matrix cores */
+    GEMM_ALGO_MFMA = 3,      /* LDS-staged macro tiles on the matrix cores, operands
+                                staged through registers (any shape and alignment) */
+    GEMM_ALGO_MFMA_DIRECT = 4 /* macro tiles fed by direct global->LDS loads (fp16/bf16,
+                                 full tiles, 16-byte aligned operands); other problems
+                                 run as GEMM_ALGO_MFMA.  AUTO uses it when eligible. */
 } gemm_algo_t;
 
 /* Tile configurations of the MFMA family (macro tile BM x BN, waves). */
@@ -95,7 +99,8 @@ typedef enum {
     GEMM_TILE_256x256 = 1, /* 4 waves, 128 x 128 per wave */
     GEMM_TILE_256x128 = 2, /* 4 waves, 128 x 64 per wave */
     GEMM_TILE_128x128 = 3, /* 4 waves, 64 x 64 per wave */
-    GEMM_TILE_128x64 = 4   /* 4 waves, 64 x 32 per wave */
+    GEMM_TILE_128x64 = 4,  /* 4 waves, 64 x 32 per wave */
+    GEMM_TILE_256x256_W8 = 5 /* 8 waves (two per SIMD), 128 x 64 per wave */
 } gemm_tile_t;
 
 typedef struct {

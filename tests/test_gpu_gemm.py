@@ -17,7 +17,7 @@ from gpu_util import assert_bits, assert_close, to_dev, bits_of
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "256x128", "128x128", "128x64"]
+TILES = ["256x256", "256x128", "128x128", "128x64", "256x256w8"]
 
 
 def _operands(M, N, K, dtype, trans_b, integer, seed):
@@ -249,3 +249,47 @@ def test_forced_launch_failure(monkeypatch):
     C = dge.gemm_f16(A, A, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.all(C == 8)
+
+
+DIRECT_TILES = ["256x256w8", "256x256", "256x128", "128x128", "128x64"]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (512, 768, 320), (256, 512, 1024)])
+def test_direct_lds_path_full_tiles(M, N, K, trans_b, dtype):
+    # full tiles and 16-byte aligned operands: the direct global->LDS kernels
+    # (a 128 x 64 tile with a K x N B runs the register-staged kernel instead)
+    Ai, Bi = _operands(M, N, K, dtype, trans_b, True, 600 + M + K)
+    Ti, _ = oracle.gemm(Ai, Bi, dtype, trans_b=trans_b)
+    A, B = _operands(M, N, K, dtype, trans_b, False, 700 + M + K)
+    T, U = oracle.gemm(A, B, dtype, trans_b=trans_b)
+    for tile in DIRECT_TILES:
+        C = _run(Ai, Bi, dtype, trans_b, torch.float32, algo="mfma_direct", tile=tile)
+        assert_bits(C, Ti, what="int %s" % tile)
+        C = _run(A, B, dtype, trans_b, torch.float16, algo="mfma_direct", tile=tile)
+        assert_close(C, T, U, what=tile)
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_direct_lds_path_split_k_and_epilogue(trans_b):
+    M, N, K = 512, 512, 2048
+    Ai, Bi = _operands(M, N, K, "f16", trans_b, True, 800)
+    Ti, _ = oracle.gemm(Ai, Bi, "f16", trans_b=trans_b)
+    ws = torch.empty(dge.gemm_workspace_size_splits(M, N, 3) // 4, dtype=torch.float32,
+                     device="cuda")
+    for splits in (2, 3):
+        C = dge.gemm_ex(to_dev(Ai, "f16"), to_dev(Bi, "f16"), trans_b=trans_b,
+                        out_dtype=torch.float32, workspace=ws, algo="mfma_direct",
+                        tile="256x256w8", splits=splits)
+        torch.cuda.synchronize()
+        assert_bits(C, Ti, what="splits=%d" % splits)
+    A, B = _operands(M, N, K, "f16", trans_b, False, 801)
+    r = np.random.Generator(np.random.PCG64(802))
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), "f16")
+    bias = oracle.decode(bias_bits, "f16")
+    T, U = oracle.gemm(A, B, "f16", trans_b=trans_b, epi="bias_gelu", bias=bias)
+    C = dge.gemm_ex(to_dev(A, "f16"), to_dev(B, "f16"), trans_b=trans_b, epi="bias_gelu",
+                    bias=to_dev(bias_bits, "f16"), algo="mfma_direct", tile="256x256w8")
+    torch.cuda.synchronize()
+    assert_close(C, T, U, bias=bias)
