@@ -65,13 +65,20 @@ def prefill_stack_tokens_per_s(t_attn, t_up, t_down, tokens=2048, layers=32):
 
 # ------------------------------------------------------------ timing
 
-def time_launches(fn, steps, warmup, torch):
-    """Run fn warmup times, then time `steps` calls.  Returns (per-call
-    durations in s from event pairs around each call, wall of the whole
-    bracket in s).  All on torch's current stream, which the binding uses."""
+def time_launches(fn, steps, warmup, torch, warm_seconds=0.3):
+    """Run fn warmup times and then for at least warm_seconds (the engine
+    clock needs a few hundred ms of load to settle), then time `steps` calls.
+    Returns (per-call durations in s from event pairs around each call, wall
+    of the whole bracket in s).  All on torch's current stream, which the
+    binding uses."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0 = time.perf_counter()
@@ -241,6 +248,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the headline GEMM")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only a plain 256 MiB device-to-device copy, 5 times (the reference "
+                         "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -250,6 +260,17 @@ def main():
     import torch
     import dense_gemm_engineering_amd.binding as dge
     from dense_gemm_engineering_amd import inputs
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                          "launches": 5}), flush=True)
+        return
 
     dge.gemm_init()
     M = N = K = 4096

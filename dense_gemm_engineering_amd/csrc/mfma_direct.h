@@ -40,9 +40,24 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
+// One global_load_lds_dwordx4: 16 bytes per lane from g to LDS address
+// (l + 16 * lane).  Issued as inline assembly on purpose: the compiler then
+// does not count it in its memory-wait bookkeeping, and every wait for these
+// loads is explicit in the kernel (s_waitcnt vmcnt before the barrier that
+// publishes a stage).  Left to the compiler, each later transposed LDS read
+// (whose intrinsic carries no address information) would be preceded by a
+// wait for ALL outstanding loads, serialising every stage with its loads.
+// M0 (the LDS base of the copy) is set inside the same statement; these
+// kernels have no other M0 user, so the clobber of that reserved register is
+// safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void lds_dma16(const void* g, DGE_LDS void* l) {
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+    const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la)
+                 : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ inline uint2 ds_read_tr(const DGE_LDS char* p) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DGE_LDS s16x4*)p);
@@ -227,3 +242,4 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
 }
 
 }  // namespace dge
+
