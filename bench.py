@@ -67,10 +67,10 @@ def prefill_stack_tokens_per_s(t_attn, t_up, t_down, tokens=2048, layers=32):
 
 def time_launches(fn, steps, warmup, torch, warm_seconds=0.3):
     """Run fn warmup times and then for at least warm_seconds (the engine
-    clock needs a few hundred ms of load to settle), then time `steps` calls.
-    Returns (per-call durations in s from event pairs around each call, wall
-    of the whole bracket in s).  All on torch's current stream, which the
-    binding uses."""
+    clock needs a few hundred ms of load to settle), then time `steps`
+    back-to-back calls between one pair of HIP events on torch's current
+    stream (the stream the binding launches on).  Returns (average GPU time
+    per call in s, host wall time of the synchronised bracket in s)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -79,17 +79,17 @@ def time_launches(fn, steps, warmup, torch, warm_seconds=0.3):
         for _ in range(20):
             fn()
         torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record()
+    e0.record()
+    for _ in range(steps):
         fn()
-        e.record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) * 1e-3 for s, e in ev]
-    return per, wall
+    return e0.elapsed_time(e1) * 1e-3 / steps, wall
 
 
 def _src_hash():
@@ -140,7 +140,7 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
     """Per shape: dequant (HBM-cold by rotating weight sets), GEMM, tok/s."""
     out = {}
     for shape in ("up", "attn", "down"):
-        A, q, N, K = inputs.cfg4(shape)
+        A, q, N, K = inputs.prefill_projection(shape)
         dA = _dev(A, "f16", torch)
         nset = max(1, int(np.ceil(rotate_bytes / dequant_alg_bytes(N, K))))
         qs = [torch.from_numpy(q).cuda() for _ in range(nset)]
@@ -158,9 +158,8 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
         def gem():
             dge.gemm_f16(dA, ws[0], C, trans_b=True, workspace=work)
 
-        t_deq, _ = time_launches(deq, steps, 3, torch)
-        t_gem, _ = time_launches(gem, steps, 3, torch)
-        td, tg = _med(t_deq), _med(t_gem)
+        td, _ = time_launches(deq, steps, 3, torch)
+        tg, _ = time_launches(gem, steps, 3, torch)
         out[shape] = {"N": N, "K": K, "dequant_us": td * 1e6, "gemm_us": tg * 1e6,
                       "dequant_GBs": dequant_alg_bytes(N, K) / td / 1e9,
                       "dequant_hbm_frac": dequant_alg_bytes(N, K) / td / 1e9 / HBM_PEAK_GBS,
@@ -180,7 +179,7 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
 def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
     out = {}
     for N in (160, 32):
-        X, W, bias = inputs.cfg5(N)
+        X, W, bias = inputs.tall_skinny(N)
         alg = gemm_alg_bytes(65536, N, 160, 2, 2, bias_bytes=2 * N)
         nset = max(1, int(np.ceil(rotate_bytes / alg)))
         Xs = [_dev(X, "f16", torch) for _ in range(nset)]
@@ -193,8 +192,7 @@ def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
             it[0] += 1
             dge.gemm_f16(Xs[i], dW, Cs[i], epi="bias_gelu", bias=db)
 
-        per, _ = time_launches(run, steps, 3, torch)
-        t = _med(per)
+        t, _ = time_launches(run, steps, 3, torch)
         out["N%d" % N] = {"us": t * 1e6, "GBs": alg / t / 1e9, "hbm_frac": alg / t / 1e9 / HBM_PEAK_GBS,
                           "TFLOPs": gemm_flops(65536, N, 160) / t / 1e12}
         del Xs, Cs
@@ -204,15 +202,15 @@ def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
 def bench_ladder(dge, inputs, torch, steps):
     out = {}
     for n in (1024, 2048, 4096):
-        A, B = inputs.cfg3(n)
+        A, B = inputs.fp32_square(n)
         dA, dB = _dev(A, "f32", torch), _dev(B, "f32", torch)
         C = torch.empty((n, n), dtype=torch.float32, device="cuda")
         row = {}
         algos = ["naive", "lds_tiled", "mfma"] if n <= 2048 else ["lds_tiled", "mfma"]
         for algo in algos:
             s = max(2, steps // 10) if algo != "mfma" else steps
-            per, _ = time_launches(lambda: dge.gemm_ex(dA, dB, C, algo=algo), s, 1, torch)
-            t = _med(per)
+            t, _ = time_launches(lambda: dge.gemm_ex(dA, dB, C, algo=algo), s, 1, torch,
+                                 warm_seconds=0.1)
             row[algo] = {"us": t * 1e6, "TFLOPs": gemm_flops(n, n, n) / t / 1e12,
                          "fp32_mfma_frac": gemm_flops(n, n, n) / t / 1e12 / PEAK["f32"]}
         out["n%d" % n] = row
@@ -220,23 +218,25 @@ def bench_ladder(dge, inputs, torch, steps):
 
 
 def cpu_baseline(A, B, seconds_target=15.0):
-    """The oracle, untuned, on all host cores: rows of the 4096^3 product."""
+    """The oracle, untuned, on all host cores: the first rows of the 4096^3
+    product (all of them when that takes at most about 2x seconds_target)."""
     import oracle
     cores = oracle.default_threads()
-    rows = 16
+    probe = max(cores, 64)
     t0 = time.perf_counter()
-    oracle.gemm(A[:rows], B, "f16", want_U=False, threads=cores)
-    t = time.perf_counter() - t0
-    # scale the sample so the measured leg takes about seconds_target
-    rows = int(min(4096, max(rows, rows * seconds_target / max(t, 1e-3))))
-    rows = max(cores, rows - rows % cores)
+    oracle.gemm(A[:probe], B, "f16", want_U=False, threads=cores)
+    tp = time.perf_counter() - t0
+    est_full = tp * 4096 / probe
+    rows = 4096 if est_full <= 2 * seconds_target else int(4096 * seconds_target / est_full)
+    rows = max(probe, rows - rows % cores)
     t0 = time.perf_counter()
     oracle.gemm(A[:rows], B, "f16", want_U=False, threads=cores)
     t = time.perf_counter() - t0
     return {"value": gemm_flops(rows, 4096, 4096) / t / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": t,
-            "sample": "rows 0..%d of the 4096^3 fp16 product (%.2f GFLOP), binary64 "
-                      "accumulation, row-parallel over %d threads" % (rows - 1, gemm_flops(rows, 4096, 4096) / 1e9, cores)}
+            "sample": "rows 0..%d of the 4096^3 fp16 product (%.1f GFLOP), binary64 "
+                      "accumulation, row-parallel over %d threads"
+                      % (rows - 1, gemm_flops(rows, 4096, 4096) / 1e9, cores)}
 
 
 def main():
@@ -253,7 +253,7 @@ def main():
                          "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -274,7 +274,7 @@ def main():
 
     dge.gemm_init()
     M = N = K = 4096
-    A, B = inputs.cfg2(args.dtype)
+    A, B = inputs.square4096(args.dtype)
     dA, dB = _dev(A, args.dtype, torch), _dev(B, args.dtype, torch)
     C = torch.empty((M, N), dtype=torch.float16, device="cuda")
     wsz = dge.gemm_workspace_size(M, N, K, dA.dtype)
@@ -282,9 +282,8 @@ def main():
     fn = (lambda: dge.gemm_f16(dA, dB, C, workspace=work)) if args.dtype == "f16" else \
         (lambda: dge.gemm_bf16(dA, dB, C, workspace=work))
 
-    per, wall = time_launches(fn, args.steps, args.warmup, torch)
+    avg_kernel, wall = time_launches(fn, args.steps, args.warmup, torch)
     flops = gemm_flops(M, N, K)
-    avg_kernel = float(np.mean(per))
     ms_per_step = wall / args.steps * 1e3
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_kernel / 1e12
@@ -301,8 +300,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[args.dtype],
                      "unit": "TFLOP/s", "frac": achieved / PEAK[args.dtype],
                      "traffic": traffic,
-                     "kernel_us_mean": avg_kernel * 1e6, "kernel_us_median": _med(per) * 1e6,
-                     "alg_bytes": gemm_alg_bytes(M, N, K, 2, 2)},
+                     "kernel_us_mean": avg_kernel * 1e6,
+                     "alg_bytes": gemm_alg_bytes(M, N, K, 2, 2),
+                     "kernel": "gemm_direct_kernel<fp16, 256x256 tile, 8 waves, K x N B>"},
     }
     if not args.no_extra:
         extra_steps = max(10, min(args.steps, 30))

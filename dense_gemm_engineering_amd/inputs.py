@@ -6,29 +6,30 @@ bfloat16 cast, both round-to-nearest-even) and packs q4 blocks in their
 storage format.  The same host arrays feed both the GPU library and the CPU
 oracle.
 
-Seeds: operand o of workload c, variant v, uses PCG64(1000*c + 10*v + o), with
+Seeds: operand o of workload w, variant v, uses PCG64(1000*w + 10*v + o), with
 o = 1 (A), 2 (B), 3 (bias), 4 (q4 scales), 5 (q4 codes), 6 (old C).
 
-Workloads (all row-major):
-  1  256^3 fp16, U[-1,1); a second pass with integers in [-4, 4]
-  2  4096^3 fp16 or bf16, N(0,1)/sqrt(K)
-  3  n^3 fp32, U[-1,1), n in {1024, 2048, 4096}
-  4  prefill: A 2048 x K fp16 N(0,1); W N x K as q4 blocks with scales
-     fp16(|N(0, 0.02)|) and codes uniform in 0..15
-  5  tall-skinny: X 65536 x 160 and W 160 x N (N = 160 or 32), both
-     N(0,1)/sqrt(160) fp16; bias fp16 N(0, 0.1)
+Workloads (all row-major; w is the seed family):
+  square256 (w=1)          256^3 fp16, U[-1,1); a second pass with integers
+                           in [-4, 4]
+  square4096 (w=2)         4096^3 fp16 or bf16, N(0,1)/sqrt(K)
+  fp32_square (w=3)        n^3 fp32, U[-1,1), n in {1024, 2048, 4096}
+  prefill_projection (w=4) A 2048 x K fp16 N(0,1); W N x K as q4 blocks with
+                           scales fp16(|N(0, 0.02)|) and codes uniform 0..15
+  tall_skinny (w=5)        X 65536 x 160 and W 160 x N (N = 160 or 32), both
+                           N(0,1)/sqrt(160) fp16; bias fp16 N(0, 0.1)
 """
 import numpy as np
 
 OP_A, OP_B, OP_BIAS, OP_SCALE, OP_CODE, OP_C = 1, 2, 3, 4, 5, 6
 
 
-def seed(config, operand, variant=0):
-    return 1000 * config + 10 * variant + operand
+def seed(workload, operand, variant=0):
+    return 1000 * workload + 10 * variant + operand
 
 
-def rng(config, operand, variant=0):
-    return np.random.Generator(np.random.PCG64(seed(config, operand, variant)))
+def rng(workload, operand, variant=0):
+    return np.random.Generator(np.random.PCG64(seed(workload, operand, variant)))
 
 
 def to_bits(x, dtype):
@@ -45,17 +46,17 @@ def to_bits(x, dtype):
     raise ValueError(dtype)
 
 
-def uniform(shape, dtype, config, operand, variant=0, lo=-1.0, hi=1.0):
-    return to_bits(rng(config, operand, variant).uniform(lo, hi, size=shape), dtype)
+def uniform(shape, dtype, workload, operand, variant=0, lo=-1.0, hi=1.0):
+    return to_bits(rng(workload, operand, variant).uniform(lo, hi, size=shape), dtype)
 
 
-def normal(shape, dtype, config, operand, variant=0, std=1.0):
-    return to_bits(rng(config, operand, variant).standard_normal(size=shape) * std, dtype)
+def normal(shape, dtype, workload, operand, variant=0, std=1.0):
+    return to_bits(rng(workload, operand, variant).standard_normal(size=shape) * std, dtype)
 
 
-def integers(shape, dtype, config, operand, variant=0, lo=-4, hi=4):
+def integers(shape, dtype, workload, operand, variant=0, lo=-4, hi=4):
     """Integer-valued entries in [lo, hi] (inclusive)."""
-    v = rng(config, operand, variant).integers(lo, hi + 1, size=shape).astype(np.float64)
+    v = rng(workload, operand, variant).integers(lo, hi + 1, size=shape).astype(np.float64)
     return to_bits(v, dtype)
 
 
@@ -76,47 +77,47 @@ def pack_q4(scale_bits, codes):
     return blk.reshape(-1)
 
 
-def q4_weights(rows, cols, config=4, variant=0, scale_std=0.02):
+def q4_weights(rows, cols, workload=4, variant=0, scale_std=0.02):
     """Synthetic q4 weight matrix (rows x cols) as raw block bytes."""
     assert cols % 32 == 0
     nb = cols // 32
-    d = np.abs(rng(config, OP_SCALE, variant).standard_normal(size=(rows, nb)) * scale_std)
+    d = np.abs(rng(workload, OP_SCALE, variant).standard_normal(size=(rows, nb)) * scale_std)
     scale_bits = to_bits(d, "f16")
-    codes = rng(config, OP_CODE, variant).integers(0, 16, size=(rows, nb, 32))
+    codes = rng(workload, OP_CODE, variant).integers(0, 16, size=(rows, nb, 32))
     return pack_q4(scale_bits, codes)
 
 
 # ----------------------------------------------------------------- workloads
 
-def cfg1(integer=False):
+def square256(integer=False):
     if integer:
         return (integers((256, 256), "f16", 1, OP_A, 1), integers((256, 256), "f16", 1, OP_B, 1))
     return uniform((256, 256), "f16", 1, OP_A), uniform((256, 256), "f16", 1, OP_B)
 
 
-def cfg2(dtype="f16", n=4096):
+def square4096(dtype="f16", n=4096):
     s = 1.0 / np.sqrt(n)
     return (normal((n, n), dtype, 2, OP_A, std=s), normal((n, n), dtype, 2, OP_B, std=s))
 
 
-def cfg3(n):
+def fp32_square(n):
     v = {1024: 0, 2048: 1, 4096: 2}.get(n, 3)
     return uniform((n, n), "f32", 3, OP_A, v), uniform((n, n), "f32", 3, OP_B, v)
 
 
-CFG4_SHAPES = {"up": (11008, 4096), "attn": (4096, 4096), "down": (4096, 11008)}
+PREFILL_SHAPES = {"up": (11008, 4096), "attn": (4096, 4096), "down": (4096, 11008)}
 
 
-def cfg4(shape="up", M=2048):
+def prefill_projection(shape="up", M=2048):
     """Prefill projection inputs: A (M x K fp16 bits), q4 weight bytes, N, K."""
-    N, K = CFG4_SHAPES[shape]
+    N, K = PREFILL_SHAPES[shape]
     v = {"up": 0, "attn": 1, "down": 2}[shape]
     A = normal((M, K), "f16", 4, OP_A, v)
     q = q4_weights(N, K, 4, v)
     return A, q, N, K
 
 
-def cfg5(N=160, M=65536, K=160):
+def tall_skinny(N=160, M=65536, K=160):
     v = 0 if N == 160 else 1
     s = 1.0 / np.sqrt(K)
     X = normal((M, K), "f16", 5, OP_A, v, std=s)

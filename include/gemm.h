@@ -69,7 +69,7 @@ extern "C" {
 typedef enum {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_VALUE = 1, /* bad size, leading dimension, pointer, enum or overlap */
-    GEMM_ERR_NOT_SUPPORTED = 2, /* valid request this build does not implement */
+    GEMM_ERR_NOT_SUPPORTED = 2, /* valid request the library does not implement */
     GEMM_ERR_WORKSPACE = 3,     /* explicit split request without enough workspace */
     GEMM_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
     GEMM_ERR_DEVICE = 5         /* no usable gfx950 device is current */

@@ -41,8 +41,8 @@ def _run(A, B, dtype, trans_b, out, **kw):
     return C
 
 
-def test_cfg1_uniform_fp32_out_every_family():
-    A, B = inputs.cfg1()
+def test_square256_uniform_fp32_out_every_family():
+    A, B = inputs.square256()
     T, U = oracle.gemm(A, B, "f16")
     for algo, tile in [("naive", "auto"), ("lds_tiled", "auto")] + [("mfma", t) for t in TILES]:
         C = _run(A, B, "f16", False, torch.float32, algo=algo, tile=tile)
@@ -50,8 +50,8 @@ def test_cfg1_uniform_fp32_out_every_family():
 
 
 @pytest.mark.parametrize("out", [torch.float32, torch.float16])
-def test_cfg1_integer_bit_exact_every_family(out):
-    A, B = inputs.cfg1(integer=True)
+def test_square256_integer_bit_exact_every_family(out):
+    A, B = inputs.square256(integer=True)
     T, _ = oracle.gemm(A, B, "f16")
     for algo, tile in [("naive", "auto"), ("lds_tiled", "auto")] + [("mfma", t) for t in TILES]:
         C = _run(A, B, "f16", False, out, algo=algo, tile=tile)

@@ -22,7 +22,7 @@ def _ws(M, N, K, dtype=torch.float16):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_square_4096_sampled_rows(dtype):
-    A, B = inputs.cfg2(dtype)
+    A, B = inputs.square4096(dtype)
     dA, dB = to_dev(A, dtype), to_dev(B, dtype)
     C = dge.gemm(dA, dB, out_dtype=torch.float16, workspace=_ws(4096, 4096, 4096))
     torch.cuda.synchronize()
@@ -45,7 +45,7 @@ def test_square_4096_integer_bit_exact_sampled_rows():
 
 @pytest.mark.parametrize("n", [1024, 2048, 4096])
 def test_fp32_ladder_sampled_rows(n):
-    A, B = inputs.cfg3(n)
+    A, B = inputs.fp32_square(n)
     dA, dB = to_dev(A, "f32"), to_dev(B, "f32")
     rows = sample_rows(n, 24, seed=n)
     T, U = oracle.gemm(A[rows], B, "f32")
@@ -76,7 +76,7 @@ def test_dequant_every_scale_times_every_code():
 
 @pytest.mark.parametrize("shape", ["up", "attn", "down"])
 def test_dequant_full_size_bit_exact(shape):
-    N, K = inputs.CFG4_SHAPES[shape]
+    N, K = inputs.PREFILL_SHAPES[shape]
     q = inputs.q4_weights(N, K, 4, {"up": 0, "attn": 1, "down": 2}[shape])
     got = dge.dequant_q4_f16(torch.from_numpy(q).cuda(), N, K)
     torch.cuda.synchronize()
@@ -101,7 +101,7 @@ def test_dequant_rejects_ragged_cols():
 
 @pytest.mark.parametrize("shape", ["up", "attn", "down"])
 def test_prefill_full_size(shape):
-    A, q, N, K = inputs.cfg4(shape)
+    A, q, N, K = inputs.prefill_projection(shape)
     dA = to_dev(A, "f16")
     w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
     C = dge.prefill_q4_f16(dA, torch.from_numpy(q).cuda(), N, K, w16=w16,
@@ -131,7 +131,7 @@ def test_prefill_tail_shape_unit_scales_exact():
 
 @pytest.mark.parametrize("N", [160, 32])
 def test_tall_skinny_bias_gelu_sampled_rows(N):
-    X, W, bias = inputs.cfg5(N)
+    X, W, bias = inputs.tall_skinny(N)
     C = dge.gemm_f16(to_dev(X, "f16"), to_dev(W, "f16"), out_dtype=torch.float16,
                      epi="bias_gelu", bias=to_dev(bias, "f16"))
     torch.cuda.synchronize()

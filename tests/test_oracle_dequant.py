@@ -49,7 +49,7 @@ def test_exhaustive_scales_times_codes():
 
 def test_multirow_addressing():
     rows, cols = 7, 96
-    q = inputs.q4_weights(rows, cols, config=90)
+    q = inputs.q4_weights(rows, cols, workload=90)
     got = oracle.dequant_q4(q, rows, cols)
     blk = q.reshape(rows, cols // 32, 18)
     for r in range(rows):

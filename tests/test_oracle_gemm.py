@@ -148,7 +148,7 @@ def test_alpha_beta_linearity_exact():
 
 
 def test_beta_zero_never_reads_c():
-    A, B = inputs.cfg1()
+    A, B = inputs.square256()
     C_old = np.full((256, 256), np.nan)
     T, _ = oracle.gemm(A[:8], B, "f16", beta=0.0, C_old=C_old[:8])
     assert np.all(np.isfinite(T))
@@ -166,7 +166,7 @@ def test_bf16_output_rounding_exceeds_1e3_by_construction():
     # Why bf16 outputs get the widened normwise bound: rounding an exact
     # result to bf16 alone already gives ~1.1e-3 normwise relative error.
     from oracle import compare
-    A, B = inputs.cfg1()
+    A, B = inputs.square256()
     T, _ = oracle.gemm(A[:64], B, "f16")
     Cb = oracle.decode(oracle.encode(T, "bf16"), "bf16")
     e = compare.normwise_rel_err(Cb, T)
