@@ -37,7 +37,7 @@ gemm_status_t current_device(DeviceInfo* out) {
         hipDeviceProp_t prop;
         DeviceInfo info{0, 0};
         if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-            std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+            std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && skinny_init() == hipSuccess) {
             info.ok = 1;
             info.cus = prop.multiProcessorCount;
         }
@@ -292,12 +292,47 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
     return launch_status(e);
 }
 
+// The tall-skinny kernel: 16-bit inputs, K a multiple of 32 up to 256,
+// N up to 256, X rows 16-byte aligned, W^T fitting 64 KB of LDS.
+bool skinny_eligible(const Gemm& g) {
+    if (g.dt == IN_F32 || g.K < 32 || g.K > 256 || g.K % 32 != 0 || g.N > 256) return false;
+    if (!aligned16(g.A) || g.lda % 8 != 0) return false;
+    const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
+    return skinny_lds_bytes(nt, (int)g.K + 8, out_bytes(g.c_type)) <= 160 * 1024;
+}
+
+gemm_status_t run_skinny(const Gemm& g, int cus) {
+    SkinnyArgs a;
+    a.X = g.A;
+    a.W = g.B;
+    a.C = g.C;
+    a.ldx = g.lda;
+    a.ldw = g.ldb;
+    a.ldc = g.ldc;
+    a.M = (int)g.M;
+    a.N = (int)g.N;
+    a.K = (int)g.K;
+    a.pitch = (int)g.K + 8;
+    a.c_type = g.c_type;
+    const int cb = out_bytes(g.c_type);
+    a.vec_c = (aligned16(g.B) && g.ldb % 8 == 0 ? 2 : 0) |
+              (aligned16(g.C) && (g.ldc * cb) % 16 == 0 && (g.N * cb) % 16 == 0 ? 4 : 0);
+    a.ep = make_epilogue(g);
+    const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
+    const size_t lds = skinny_lds_bytes(nt, a.pitch, cb);
+    const int rows_per_wg = SKINNY_WAVES * skinny_rb(nt) * 16;
+    // one workgroup per CU: W is staged once per CU and amortised over the
+    // CU's share of the rows
+    const int grid = std::max(1, std::min(ceil_div(g.M, rows_per_wg), cus));
+    return launch_status(launch_skinny(g.dt, nt, g.trans_b, a, grid, lds, g.stream));
+}
+
 gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
     gemm_status_t st = validate(g);
     if (st != GEMM_OK) return st;
     gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
     if (tuning) tn = *tuning;
-    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_MFMA_DIRECT) return GEMM_ERR_INVALID_VALUE;
+    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_SKINNY) return GEMM_ERR_INVALID_VALUE;
     if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8) return GEMM_ERR_INVALID_VALUE;
     if (tn.splits < 0) return GEMM_ERR_INVALID_VALUE;
     if (g.M == 0 || g.N == 0) return GEMM_OK;
@@ -313,6 +348,15 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
             return launch_status(launch_lds_tiled(g.dt, simple_args(g), g.stream));
         case GEMM_ALGO_MFMA:
             return run_mfma(g, tn.tile, tn.splits, dev.cus, 0);
+        case GEMM_ALGO_SKINNY:
+            if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
+            if (skinny_eligible(g)) return run_skinny(g, dev.cus);
+            return run_mfma(g, tn.tile, 1, dev.cus, 1);
+        case GEMM_ALGO_AUTO:
+            if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && skinny_eligible(g) &&
+                g.M >= 8 * g.N && g.M >= 4096 && env_int("GEMM_SKINNY", 1) != 0)
+                return run_skinny(g, dev.cus);
+            return run_mfma(g, tn.tile, tn.splits, dev.cus, 1);
         default:
             return run_mfma(g, tn.tile, tn.splits, dev.cus, 1);
     }

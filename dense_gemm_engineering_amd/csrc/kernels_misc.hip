@@ -57,11 +57,12 @@ hipError_t launch_splitk_fixup(int dt, const SimpleArgs& a, const float* ws, int
 
 hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
                              int vec_out, hipStream_t s) {
-    const int64_t total = rows * (cols / 8);
-    int64_t blocks = (total + 255) / 256;
+    const int64_t total = rows * (cols / 32);
+    int64_t blocks = (total + DQ_BLOCKS - 1) / DQ_BLOCKS;
     if (blocks > 1 << 20) blocks = 1 << 20;
+    const int flags = (((uintptr_t)q & 15) == 0 ? 1 : 0) | (vec_out ? 2 : 0);
     hipLaunchKernelGGL(dequant_q4_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, vec_out);
+                       (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
     return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 #include "device_common.h"
 #include "ladder.h"
 #include "mfma_gemm.h"
+#include "skinny.h"
 
 namespace dge {
 
@@ -45,6 +46,14 @@ hipError_t launch_mfma_f32(int tile, int trans_b, int fast, const MfmaArgs& a, i
 hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, hipStream_t s);
 hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg,
                                    hipStream_t s);
+
+// Tall-skinny kernel: nt = 16-column tiles of N (even, 2..16), lds = dynamic
+// LDS bytes (nt * 16 rows of W^T at the args' pitch).
+hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid, size_t lds,
+                         hipStream_t s);
+// Allows every skinny instance up to 160 KB of dynamic LDS.  Called once per
+// device at library initialisation, never from inside a launch sequence.
+hipError_t skinny_init();
 
 hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s);
 hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s);

@@ -88,9 +88,14 @@ typedef enum {
     GEMM_ALGO_LDS_TILED = 2, /* LDS tiles + register-blocked fp32 FMA, no matrix cores */
     GEMM_ALGO_MFMA = 3,      /* LDS-staged macro tiles on the matrix cores, operands
                                 staged through registers (any shape and alignment) */
-    GEMM_ALGO_MFMA_DIRECT = 4 /* macro tiles fed by direct global->LDS loads (fp16/bf16,
-                                 full tiles, 16-byte aligned operands); other problems
-                                 run as GEMM_ALGO_MFMA.  AUTO uses it when eligible. */
+    GEMM_ALGO_MFMA_DIRECT = 4, /* macro tiles fed by direct global->LDS loads (fp16/bf16,
+                                  full tiles, 16-byte aligned operands); other problems
+                                  run as GEMM_ALGO_MFMA.  AUTO uses it when eligible. */
+    GEMM_ALGO_SKINNY = 5      /* tall-skinny kernel: W resident in LDS, X streamed into
+                                 the MFMA operands (fp16/bf16, K a multiple of 32 up to
+                                 256, N <= 256, A 16-byte aligned with lda % 8 == 0);
+                                 other problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO uses
+                                 it for M >= 4096 and M >= 8N when eligible. */
 } gemm_algo_t;
 
 /* Tile configurations of the MFMA family (macro tile BM x BN, waves). */

@@ -293,3 +293,34 @@ def test_direct_lds_path_split_k_and_epilogue(trans_b):
                     bias=to_dev(bias_bits, "f16"), algo="mfma_direct", tile="256x256w8")
     torch.cuda.synchronize()
     assert_close(C, T, U, bias=bias)
+
+
+SKINNY_SHAPES = [(5000, 160, 160), (4096, 32, 160), (1000, 70, 96), (300, 256, 256), (77, 16, 32),
+                 (2050, 200, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_kernel(M, N, K, trans_b, dtype):
+    Ai, Bi = _operands(M, N, K, dtype, trans_b, True, 900 + M + N)
+    Ti, _ = oracle.gemm(Ai, Bi, dtype, trans_b=trans_b)
+    for out in (torch.float32, torch.float16):
+        C = _run(Ai, Bi, dtype, trans_b, out, algo="skinny")
+        assert_bits(C, Ti, what="int %s" % out)
+    A, B = _operands(M, N, K, dtype, trans_b, False, 950 + M + N)
+    r = np.random.Generator(np.random.PCG64(951))
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), dtype)
+    bias = oracle.decode(bias_bits, dtype)
+    cold_bits = inputs.to_bits(r.uniform(-1, 1, (M, N)), "f16")
+    cold = oracle.decode(cold_bits, "f16")
+    for epi in ("none", "bias_gelu"):
+        beta = 0.5 if epi == "none" else 0.0
+        T, U = oracle.gemm(A, B, dtype, trans_b=trans_b, alpha=1.25, beta=beta, C_old=cold,
+                           epi=epi, bias=bias)
+        C = to_dev(cold_bits, "f16")
+        dge.gemm_ex(to_dev(A, dtype), to_dev(B, dtype), C, trans_b=trans_b, alpha=1.25, beta=beta,
+                    epi=epi, bias=to_dev(bias_bits, dtype) if epi != "none" else None,
+                    algo="skinny")
+        torch.cuda.synchronize()
+        assert_close(C, T, U, 1.25, beta, cold, bias if epi != "none" else None, what=epi)
