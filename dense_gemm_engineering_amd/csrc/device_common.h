@@ -13,6 +13,7 @@ enum : int { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 enum : int { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU = 2 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

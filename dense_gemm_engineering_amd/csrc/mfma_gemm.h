@@ -290,10 +290,58 @@ __device__ inline void finish_row8(const MfmaArgs& p, int row, int col, const fl
     store_row8<OT>(p.C, p.ldc, row, col, p.N, t, vec);
 }
 
-// ---- a4: the fused epilogue of one workgroup tile.  Each wave stages its
-// accumulators through LDS 16 rows at a time (stg: NW x 16 x (WTN + 4) fp32)
-// and writes 8 consecutive columns per lane, so a wave stores whole rows;
-// with a split-K workspace the raw fp32 partials go there instead.
+// ---- a4: the fused epilogue.  Each wave stages its accumulators through
+// LDS one strip of SM rows at a time and then writes 8 consecutive columns
+// per lane, so a wave stores whole rows; with a split-K workspace the raw
+// fp32 partials go there instead.  drain_strip writes one staged strip
+// (SM rows x WTN columns, row pitch PITCH floats) whose first element is
+// C[grow0][gcol0].
+template <int DT, int MODE, int WTN, int SM, int PITCH>
+__device__ inline void drain_strip(const MfmaArgs& p, const float* stg, int grow0, int gcol0,
+                                   int split, int lane) {
+    constexpr int LPR = WTN / 8;   // lanes per row, 8 columns each
+    constexpr int RPP = 64 / LPR;  // rows per pass
+    static_assert(LPR * 8 == WTN && RPP * LPR == 64 && SM % RPP == 0, "epilogue lane map");
+    // The read-back loop does not touch the accumulators; keeping it rolled
+    // keeps the strip loop small enough to unroll fully, so the accumulator
+    // array is only ever indexed statically (no scratch).
+#pragma nounroll
+    for (int pass = 0; pass < SM / RPP; ++pass) {
+        const int r = pass * RPP + lane / LPR;
+        const int c8 = (lane % LPR) * 8;
+        const int grow = grow0 + r;
+        const int gcol = gcol0 + c8;
+        float v[8];
+        const f32x4 lo = *(const f32x4*)&stg[r * PITCH + c8];
+        const f32x4 hi = *(const f32x4*)&stg[r * PITCH + c8 + 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = lo[e];
+            v[4 + e] = hi[e];
+        }
+        if (MODE == LOAD_EDGE && (grow >= p.M || gcol >= p.N)) continue;
+        if (p.ws) {
+            float* w = p.ws + ((int64_t)split * p.M + grow) * p.N + gcol;
+            if (p.vec_ok && gcol + 8 <= p.N && (p.N & 3) == 0) {
+                *(f32x4*)w = lo;
+                *(f32x4*)(w + 4) = hi;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (gcol + e < p.N) w[e] = v[e];
+            }
+        } else if (p.c_type == OUT_F16) {
+            finish_row8<DT, OUT_F16>(p, grow, gcol, v);
+        } else if (p.c_type == OUT_BF16) {
+            finish_row8<DT, OUT_BF16>(p, grow, gcol, v);
+        } else {
+            finish_row8<DT, OUT_F32>(p, grow, gcol, v);
+        }
+    }
+}
+
+// Epilogue of a tile held as 16x16 accumulator blocks (16-row strips,
+// stg: NW x 16 x (WTN + 4) fp32).
 template <int DT, int BM, int BN, int WM, int WN, int MODE, int TM, int TN>
 __device__ inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], float* stg_all,
                                      int m0, int n0, int split) {
@@ -303,10 +351,6 @@ __device__ inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], fl
     const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
     constexpr int PITCH = WTN + 4;  // floats; the pad staggers rows across banks
     float* stg = stg_all + wave * (16 * PITCH);
-    constexpr int LPR = WTN / 8;  // lanes per row, 8 columns each
-    constexpr int RPP = 64 / LPR; // rows per pass
-    static_assert(LPR * 8 == WTN && RPP * LPR == 64 && 16 % RPP == 0, "epilogue lane map");
-
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -315,42 +359,34 @@ __device__ inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], fl
             for (int e = 0; e < 4; ++e)
                 stg[(4 * (lane >> 4) + e) * PITCH + 16 * j + (lane & 15)] = acc[i][j][e];
         __syncthreads();
-        // The read-back loop does not touch the accumulators; keeping it
-        // rolled keeps the strip loop small enough to unroll fully, so the
-        // accumulator array is only ever indexed statically (no scratch).
-#pragma nounroll
-        for (int pass = 0; pass < 16 / RPP; ++pass) {
-            const int r = pass * RPP + lane / LPR;
-            const int c8 = (lane % LPR) * 8;
-            const int grow = m0 + wm0 + 16 * i + r;
-            const int gcol = n0 + wn0 + c8;
-            float v[8];
-            const f32x4 lo = *(const f32x4*)&stg[r * PITCH + c8];
-            const f32x4 hi = *(const f32x4*)&stg[r * PITCH + c8 + 4];
+        drain_strip<DT, MODE, WTN, 16, PITCH>(p, stg, m0 + wm0 + 16 * i, n0 + wn0, split, lane);
+        __syncthreads();
+    }
+}
+
+// Epilogue of a tile held as 32x32 accumulator blocks: lane l holds rows
+// 8 (r / 4) + 4 (l / 32) + r % 4, r = 0..15, of column l % 32.  32-row
+// strips, stg: NW x 32 x (WTN + 8) fp32 (the pad puts the two row halves a
+// lane group writes in different banks).
+template <int DT, int BM, int BN, int WM, int WN, int MODE, int TM, int TN>
+__device__ inline void epilogue_tile32(const MfmaArgs& p, f32x16 (&acc)[TM][TN], float* stg_all,
+                                       int m0, int n0, int split) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
+    constexpr int PITCH = WTN + 8;
+    float* stg = stg_all + wave * (32 * PITCH);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = lo[e];
-                v[4 + e] = hi[e];
-            }
-            if (MODE == LOAD_EDGE && (grow >= p.M || gcol >= p.N)) continue;
-            if (p.ws) {
-                float* w = p.ws + ((int64_t)split * p.M + grow) * p.N + gcol;
-                if (p.vec_ok && gcol + 8 <= p.N && (p.N & 3) == 0) {
-                    *(f32x4*)w = lo;
-                    *(f32x4*)(w + 4) = hi;
-                } else {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gcol + e < p.N) w[e] = v[e];
-                }
-            } else if (p.c_type == OUT_F16) {
-                finish_row8<DT, OUT_F16>(p, grow, gcol, v);
-            } else if (p.c_type == OUT_BF16) {
-                finish_row8<DT, OUT_BF16>(p, grow, gcol, v);
-            } else {
-                finish_row8<DT, OUT_F32>(p, grow, gcol, v);
-            }
-        }
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                stg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * j + (lane & 31)] =
+                    acc[i][j][r];
+        __syncthreads();
+        drain_strip<DT, MODE, WTN, 32, PITCH>(p, stg, m0 + wm0 + 32 * i, n0 + wn0, split, lane);
         __syncthreads();
     }
 }
