@@ -165,50 +165,76 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // relative to the 8-wave 256 x 256 tile (measured on MI355X at 4096^3, fp16,
 // direct-to-LDS path): one wave per SIMD cannot keep the MFMA pipe busy,
 // so the 4-wave 256-wide tiles lag; 128 x 128 runs two workgroups per CU.
-double tile_efficiency(int tile) {
-    switch (tile) {
-        case TILE_256x256_W8: return 1.0;
-        case TILE_256x256: return 0.7;
-        case TILE_256x128: return 0.55;
-        case TILE_128x128: return 0.72;
-        default: return 0.5;
-    }
-}
 int tile_occupancy(int tile) {
     return tile == TILE_256x256 || tile == TILE_256x128 || tile == TILE_256x256_W8 ? 1 : 2;
 }
 
-// Pick the tile that minimises rounds x (work of the tiles a CU runs per
-// round) / efficiency.
-int choose_tile(int64_t M, int64_t N, int cus) {
-    int best = TILE_256x256_W8;
-    double best_cost = 1e300;
-    for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
-        const TileShape ts = tile_shape(t);
-        const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
-        const int64_t slots = (int64_t)cus * tile_occupancy(t);
-        const int64_t rounds = (tiles + slots - 1) / slots;
-        const double cost =
-            (double)rounds * tile_occupancy(t) * ts.bm * ts.bn / tile_efficiency(t);
-        if (cost < best_cost * 0.999) {
-            best_cost = cost;
-            best = t;
-        }
+// Time model of one round (every CU running tile_occupancy tiles at once) of
+// a tile shape: fixed_us (prologue, epilogue, launch) + us_per_k * K.
+// Calibrated on 16-bit 4096^3 and 2048 x {4096, 11008} x {4096, 11008}
+// products with the direct-to-LDS kernels (4096^3: the 8-wave 256 x 256 tile
+// takes ~116 us, the 4-wave one ~130 us, 256 x 128 and 128 x 128 ~146-151 us
+// over two rounds).
+struct TileCost {
+    double fixed_us, us_per_k;
+};
+TileCost tile_cost(int tile) {
+    switch (tile) {
+        case TILE_256x256_W8: return {15.0, 0.0246};
+        case TILE_256x256: return {17.0, 0.0276};
+        case TILE_256x128: return {10.0, 0.0160};
+        case TILE_128x128: return {10.0, 0.0160};
+        default: return {8.0, 0.0110};  // 128 x 64
     }
-    return best;
 }
 
-// Split K when the tiles cannot fill the chip and each slice still has
-// enough K to amortise its prologue and the fixup pass.
-int choose_splits(int64_t M, int64_t N, int64_t K, int tile, int dt, int cus) {
+size_t ws_bytes_for(int64_t M, int64_t N, int splits);
+
+// Modelled time of a (tile, splits) schedule: rounds of the tile grid times
+// the per-round cost of its K slice, plus for a split the fixup pass that
+// re-reads the fp32 partials (at ~5 TB/s).  A partly filled last round runs
+// faster per tile (fewer CUs share power and bandwidth): measured ~0.75-0.8x
+// of a full round at a third to a half of the CUs, modelled as 0.65 + 0.35 f
+// for a fill fraction f.
+double schedule_us(int64_t M, int64_t N, int64_t K, int tile, int splits, int bk, int cus) {
     const TileShape ts = tile_shape(tile);
-    const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+    const TileCost c = tile_cost(tile);
+    const int64_t work = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn) * splits;
     const int64_t slots = (int64_t)cus * tile_occupancy(tile);
-    if (tiles * 2 > slots) return 1;
-    int s = (int)std::min<int64_t>(slots / tiles, 8);
-    const int64_t min_k = 16 * stage_k(dt);
-    while (s > 1 && K / s < min_k) --s;
-    return std::max(s, 1);
+    const int64_t full = work / slots, rest = work - full * slots;
+    const int64_t k_slice = (int64_t)ceil_div(ceil_div(K, bk), splits) * bk;
+    const double round_us = c.fixed_us + c.us_per_k * (double)k_slice;
+    double us = (double)full * round_us;
+    if (rest > 0) us += round_us * (0.65 + 0.35 * (double)rest / (double)slots);
+    if (splits > 1) us += (double)(4 * splits + 4) * (double)M * (double)N / 5.0e6;
+    return us;
+}
+
+// Joint choice of tile shape and K split.  tile / splits: the caller's
+// request (GEMM_TILE_AUTO / 0 = free).  A split is only considered while
+// ws_bytes covers its partials; each K slice keeps at least 16 stages.
+void choose_schedule(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
+                     int* tile, int* splits) {
+    const int bk = stage_k(dt);
+    const int t_lo = *tile == GEMM_TILE_AUTO ? TILE_256x256 : *tile;
+    const int t_hi = *tile == GEMM_TILE_AUTO ? TILE_LAST : *tile;
+    int best_t = t_lo, best_s = 1;
+    double best = 1e300;
+    for (int t = t_lo; t <= t_hi; ++t) {
+        for (int sp = 1; sp <= 8; ++sp) {
+            if (*splits > 0 && sp != *splits) continue;
+            if (sp > 1 && (K / sp < 16 * (int64_t)bk || ws_bytes < ws_bytes_for(M, N, sp)))
+                continue;
+            const double us = schedule_us(M, N, K, t, sp, bk, cus);
+            if (us < best * 0.999) {
+                best = us;
+                best_t = t;
+                best_s = sp;
+            }
+        }
+    }
+    *tile = best_t;
+    if (*splits == 0) *splits = best_s;
 }
 
 size_t ws_bytes_for(int64_t M, int64_t N, int splits) {
@@ -223,13 +249,14 @@ gemm_status_t launch_status(hipError_t e) {
 // direct: 0 = register-staged kernel only, 1 = direct-to-LDS kernel when the
 // problem qualifies (full tiles, 16-bit inputs, aligned operands).
 gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct) {
-    if (tile == GEMM_TILE_AUTO) tile = choose_tile(g.M, g.N, cus);
-    if (tile < TILE_256x256 || tile > TILE_LAST) return GEMM_ERR_INVALID_VALUE;
+    if (tile != GEMM_TILE_AUTO && (tile < TILE_256x256 || tile > TILE_LAST))
+        return GEMM_ERR_INVALID_VALUE;
+    const bool explicit_split = splits > 1;
+    if (tile == GEMM_TILE_AUTO || splits == 0)
+        choose_schedule(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, &tile, &splits);
     const TileShape ts = tile_shape(tile);
     const int bk = stage_k(g.dt);
     const int max_splits = std::max(1, ceil_div(g.K, bk));
-    bool explicit_split = splits > 1;
-    if (splits == 0) splits = choose_splits(g.M, g.N, g.K, tile, g.dt, cus);
     if (splits > max_splits) splits = max_splits;
     if (splits > 1) {
         const size_t need = ws_bytes_for(g.M, g.N, splits);
@@ -293,12 +320,13 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
 }
 
 // The tall-skinny kernel: 16-bit inputs, K a multiple of 32 up to 256,
-// N up to 256, X rows 16-byte aligned, W^T fitting 64 KB of LDS.
+// N up to 256, X rows 16-byte aligned, W^T and the staging of at least two
+// waves fitting 160 KB of LDS.
 bool skinny_eligible(const Gemm& g) {
     if (g.dt == IN_F32 || g.K < 32 || g.K > 256 || g.K % 32 != 0 || g.N > 256) return false;
     if (!aligned16(g.A) || g.lda % 8 != 0) return false;
     const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
-    return skinny_lds_bytes(nt, (int)g.K + 8, out_bytes(g.c_type)) <= 160 * 1024;
+    return skinny_lds_bytes(nt, (int)g.K + 8, out_bytes(g.c_type), 2) <= 160 * 1024;
 }
 
 gemm_status_t run_skinny(const Gemm& g, int cus) {
@@ -319,12 +347,12 @@ gemm_status_t run_skinny(const Gemm& g, int cus) {
               (aligned16(g.C) && (g.ldc * cb) % 16 == 0 && (g.N * cb) % 16 == 0 ? 4 : 0);
     a.ep = make_epilogue(g);
     const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
-    const size_t lds = skinny_lds_bytes(nt, a.pitch, cb);
-    const int rows_per_wg = SKINNY_WAVES * skinny_rb(nt) * 16;
+    const int waves = skinny_waves(nt, a.pitch, cb);
+    const size_t lds = skinny_lds_bytes(nt, a.pitch, cb, waves);
     // one workgroup per CU: W is staged once per CU and amortised over the
-    // CU's share of the rows
-    const int grid = std::max(1, std::min(ceil_div(g.M, rows_per_wg), cus));
-    return launch_status(launch_skinny(g.dt, nt, g.trans_b, a, grid, lds, g.stream));
+    // CU's share of the rows (16 * skinny_rb per wave per step)
+    const int grid = std::max(1, std::min(ceil_div(g.M, waves * 16 * skinny_rb(nt)), cus));
+    return launch_status(launch_skinny(g.dt, nt, g.trans_b, a, grid, waves, lds, g.stream));
 }
 
 gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
@@ -476,8 +504,8 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || dtype < IN_F16 || dtype > IN_F32) return 0;
     DeviceInfo dev{1, 256};
     if (current_device(&dev) != GEMM_OK) dev.cus = 256;
-    const int tile = choose_tile(M, N, dev.cus);
-    int s = choose_splits(M, N, K, tile, dtype, dev.cus);
+    int tile = GEMM_TILE_AUTO, s = 0;
+    choose_schedule(M, N, K, dtype, dev.cus, (size_t)-1, &tile, &s);
     return ws_bytes_for(M, N, s);
 }
 

@@ -72,14 +72,17 @@ template <> struct OutType<OUT_BF16> {
 };
 
 // tanh form of GELU: 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))), in fp32.
-// tanh(u) = 1 - 2 / (1 + e^{2u}), evaluated with the device exp; the result
-// saturates correctly (e^{2u} -> inf gives 1, -> 0 gives -1).  The hardware
-// reciprocal (about 1 ulp) is ample for a value that is rounded to 16 bits.
+// With 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}) this is t / (1 + 2^x),
+// x = -2 log2(e) sqrt(2/pi) (t + 0.044715 t^3) = t (C1 + C2 t^2): three
+// multiply-adds, the hardware exp2 and reciprocal (about 1 ulp each, ample
+// for a value rounded to 16 bits) and a final product.  It saturates
+// correctly: 2^x -> inf gives t * 0 = -0 for large negative t, 2^x -> 0
+// gives t.
 __device__ inline float gelu_tanh(float t) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    float u = c * (t + 0.044715f * t * t * t);
-    float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(2.0f * u));
-    return 0.5f * t * (1.0f + th);
+    constexpr float C1 = -2.3022082f;   // -2 log2(e) sqrt(2/pi)
+    constexpr float C2 = -0.10294324f;  // C1 * 0.044715
+    const float x = t * __builtin_fmaf(C2, t * t, C1);
+    return t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
 
 // Epilogue parameters, passed by value to every kernel that ends in C.

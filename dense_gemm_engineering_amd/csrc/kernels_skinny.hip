@@ -5,29 +5,29 @@
 namespace dge {
 
 template <int DT, int NT>
-static hipError_t skinny_nt(int trans_b, const SkinnyArgs& a, int grid, size_t lds,
+static hipError_t skinny_nt(int trans_b, const SkinnyArgs& a, int grid, int waves, size_t lds,
                             hipStream_t s) {
     if (trans_b)
-        hipLaunchKernelGGL((gemm_skinny_kernel<DT, NT, true>), dim3(grid), dim3(SKINNY_WAVES * 64),
-                           lds, s, a);
+        hipLaunchKernelGGL((gemm_skinny_kernel<DT, NT, true>), dim3(grid), dim3(waves * 64), lds,
+                           s, a);
     else
-        hipLaunchKernelGGL((gemm_skinny_kernel<DT, NT, false>), dim3(grid), dim3(SKINNY_WAVES * 64),
-                           lds, s, a);
+        hipLaunchKernelGGL((gemm_skinny_kernel<DT, NT, false>), dim3(grid), dim3(waves * 64), lds,
+                           s, a);
     return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t skinny_dt(int nt, int trans_b, const SkinnyArgs& a, int grid, size_t lds,
-                            hipStream_t s) {
+static hipError_t skinny_dt(int nt, int trans_b, const SkinnyArgs& a, int grid, int waves,
+                            size_t lds, hipStream_t s) {
     switch (nt) {
-        case 2: return skinny_nt<DT, 2>(trans_b, a, grid, lds, s);
-        case 4: return skinny_nt<DT, 4>(trans_b, a, grid, lds, s);
-        case 6: return skinny_nt<DT, 6>(trans_b, a, grid, lds, s);
-        case 8: return skinny_nt<DT, 8>(trans_b, a, grid, lds, s);
-        case 10: return skinny_nt<DT, 10>(trans_b, a, grid, lds, s);
-        case 12: return skinny_nt<DT, 12>(trans_b, a, grid, lds, s);
-        case 14: return skinny_nt<DT, 14>(trans_b, a, grid, lds, s);
-        case 16: return skinny_nt<DT, 16>(trans_b, a, grid, lds, s);
+        case 2: return skinny_nt<DT, 2>(trans_b, a, grid, waves, lds, s);
+        case 4: return skinny_nt<DT, 4>(trans_b, a, grid, waves, lds, s);
+        case 6: return skinny_nt<DT, 6>(trans_b, a, grid, waves, lds, s);
+        case 8: return skinny_nt<DT, 8>(trans_b, a, grid, waves, lds, s);
+        case 10: return skinny_nt<DT, 10>(trans_b, a, grid, waves, lds, s);
+        case 12: return skinny_nt<DT, 12>(trans_b, a, grid, waves, lds, s);
+        case 14: return skinny_nt<DT, 14>(trans_b, a, grid, waves, lds, s);
+        case 16: return skinny_nt<DT, 16>(trans_b, a, grid, waves, lds, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -60,10 +60,10 @@ hipError_t skinny_init() {
     return e == hipSuccess ? optin_dt<IN_BF16>() : e;
 }
 
-hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid, size_t lds,
-                         hipStream_t s) {
-    return dt == IN_BF16 ? skinny_dt<IN_BF16>(nt, trans_b, a, grid, lds, s)
-                         : skinny_dt<IN_F16>(nt, trans_b, a, grid, lds, s);
+hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid, int waves,
+                         size_t lds, hipStream_t s) {
+    return dt == IN_BF16 ? skinny_dt<IN_BF16>(nt, trans_b, a, grid, waves, lds, s)
+                         : skinny_dt<IN_F16>(nt, trans_b, a, grid, waves, lds, s);
 }
 
 }  // namespace dge

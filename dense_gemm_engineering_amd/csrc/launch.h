@@ -47,10 +47,10 @@ hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int 
 hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg,
                                    hipStream_t s);
 
-// Tall-skinny kernel: nt = 16-column tiles of N (even, 2..16), lds = dynamic
-// LDS bytes (nt * 16 rows of W^T at the args' pitch).
-hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid, size_t lds,
-                         hipStream_t s);
+// Tall-skinny kernel: nt = 16-column tiles of N (even, 2..16), waves per
+// workgroup (1..16), lds = dynamic LDS bytes (skinny_lds_bytes).
+hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid, int waves,
+                         size_t lds, hipStream_t s);
 // Allows every skinny instance up to 160 KB of dynamic LDS.  Called once per
 // device at library initialisation, never from inside a launch sequence.
 hipError_t skinny_init();

@@ -4,20 +4,23 @@
 // (X is read once, C written once; W is 51 KB), so the kernel is built around
 // streaming X:
 //
-//  * W is small enough to sit in LDS for the whole kernel, stored transposed
-//    ([n][k], k-contiguous, rows padded by 16 bytes) so that it can serve as
-//    the MFMA "A" operand of C^T = W^T X^T.
+//  * One workgroup per CU with 8 waves.  W sits in LDS once per workgroup
+//    for the whole kernel, stored transposed ([n][k], k-contiguous, rows
+//    padded by 16 bytes) so that it can serve as the MFMA "A" operand of
+//    C^T = W^T X^T; the bias is staged next to it as fp32.  A wave reads all
+//    the W^T fragments of a 32-deep k-block at once (so their LDS latencies
+//    overlap) and, up to N = 160, applies each to two 16-row blocks.
 //  * X needs no LDS: the MFMA "B" operand of X^T is 8 consecutive k of one
 //    row of X per lane, i.e. a 16-byte load straight from memory into the
-//    operand registers.  Each wave issues all the loads of its 32 rows
-//    (K / 32 k-blocks x 2 row blocks; 16 rows for N > 160) before its first
-//    MFMA, and the next rows' loads before its epilogue, so many bytes are
-//    in flight per CU.
+//    operand registers.  Each wave owns 32 rows (16 for N > 160) at a time
+//    and issues their loads (K / 32 per lane and row block) before its first
+//    MFMA, and the next rows' loads before its epilogue.  The prologue asks
+//    for W and the bias before X and publishes W with an LDS-only barrier,
+//    so each wave starts as soon as its own rows arrive.
 //  * In C^T each lane holds 4 consecutive columns n of one row m of C, so the
 //    epilogue (alpha/beta, per-column bias, tanh-GELU, rounding) works on 4
 //    adjacent outputs; the rounded tile goes through the wave's LDS staging
-//    area and leaves as whole rows, 16 bytes per lane (stores of 32-byte
-//    fragments into 16 rows at a time left HBM with partial lines).
+//    area and leaves as whole rows, 16 bytes per lane.
 #pragma once
 
 #include "device_common.h"
@@ -38,11 +41,32 @@ struct SkinnyArgs {
     Epilogue ep;
 };
 
-constexpr int SKINNY_KBMAX = 8;   // K <= 256
-constexpr int SKINNY_WAVES = 4;
-// 16-row blocks per wave: two while the accumulators of N <= 160 leave room,
-// one for wider N (keeps every instance free of register spills)
+constexpr int SKINNY_KBMAX = 8;        // K <= 256
+// 16-row blocks per wave: two while the accumulators leave room (N <= 160),
+// else one.
 __host__ __device__ constexpr int skinny_rb(int nt) { return nt <= 10 ? 2 : 1; }
+// k-blocks of X (32 k each) held in registers at a time: all of K <= 256,
+// or 5 (K <= 160 in one round trip) for N = 160 with two row blocks.  A K
+// with more k-blocks than this takes a second round trip per step.
+__host__ __device__ constexpr int skinny_kch(int nt) { return nt >= 8 && nt <= 10 ? 5 : 8; }
+// Waves per workgroup at most (256 registers per lane).
+__host__ __device__ constexpr int skinny_max_waves(int) { return 8; }
+
+// Dynamic LDS: W^T (NT*16 rows x pitch halves), the bias (NT*16 fp32), then
+// one output staging tile per wave (RB*16 rows x (NT*16*out_bytes + 16) bytes).
+__host__ __device__ inline size_t skinny_stage_bytes(int nt, int out_bytes) {
+    return (size_t)16 * skinny_rb(nt) * (nt * 16 * out_bytes + 16);
+}
+__host__ __device__ inline size_t skinny_lds_bytes(int nt, int pitch, int out_bytes, int waves) {
+    return (size_t)nt * 16 * pitch * 2 + (size_t)nt * 16 * 4 +
+           (size_t)waves * skinny_stage_bytes(nt, out_bytes);
+}
+// Waves per workgroup: the most (8, 4, 2 or 1) whose staging fits 160 KB.
+inline int skinny_waves(int nt, int pitch, int out_bytes) {
+    int w = skinny_max_waves(nt);
+    while (w > 1 && skinny_lds_bytes(nt, pitch, out_bytes, w) > 160 * 1024) w /= 2;
+    return w;
+}
 
 template <int OT>
 __device__ inline void skinny_load4(const SkinnyArgs& p, int m, int n0, float* t) {
@@ -52,16 +76,18 @@ __device__ inline void skinny_load4(const SkinnyArgs& p, int m, int n0, float* t
     for (int e = 0; e < 4; ++e) t[e] = n0 + e < p.N ? OutType<OT>::to_f32(c[e]) : 0.0f;
 }
 
-// Epilogue of one wave's RB x 16 rows: alpha/beta, bias, GELU and rounding
-// in registers (4 consecutive columns per lane), the rounded values staged in
-// the wave's LDS tile (rows of pitch_o bytes), then written out row by row
-// with 16-byte stores so that a wave writes whole rows of C.
-template <int DT, int OT, int NT, int RB>
-__device__ inline void skinny_finish(const SkinnyArgs& p, f32x4 (&acc)[RB][NT], int base,
-                                     int lane, char* stage) {
+// Epilogue of one wave's RB x 16 rows starting at row base: alpha/beta,
+// bias, GELU and rounding in registers (4 consecutive columns per lane), the
+// rounded values staged in the wave's LDS tile (rows of pitch_o bytes), then
+// written out row by row with 16-byte stores so that a wave writes whole
+// rows of C.
+template <int OT, int NT, int RB>
+__device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB][NT],
+                                     const float* bias_s, int base, int lane, char* stage) {
     typedef typename OutType<OT>::T T;
     constexpr int OB = OutType<OT>::BYTES;
-    const int pitch_o = NT * 16 * OB + 16;
+    constexpr int pitch_o = NT * 16 * OB + 16;
+    const bool has_bias = p.ep.epi != EPI_NONE, gelu = p.ep.epi == EPI_BIAS_GELU;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int ml = rb * 16 + (lane & 15);
@@ -71,11 +97,14 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, f32x4 (&acc)[RB][NT], 
             const int n0 = nt * 16 + 4 * (lane >> 4);
             float old[4] = {0.f, 0.f, 0.f, 0.f};
             if (p.ep.beta != 0.0f && m < p.M && n0 < p.N) skinny_load4<OT>(p, m, n0, old);
+            const f32x4 b = *(const f32x4*)(bias_s + n0);  // zero past N
             float t[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int n = n0 + e < p.N ? n0 + e : p.N - 1;
-                t[e] = apply_epilogue<DT>(p.ep, acc[rb][nt][e], old[e], n);
+                float v = p.ep.alpha * acc[rb][nt][e];
+                if (p.ep.beta != 0.0f) v += p.ep.beta * old[e];
+                if (has_bias) v += b[e];
+                t[e] = gelu ? gelu_tanh(v) : v;
             }
             char* dst = stage + ml * pitch_o + n0 * OB;
             if constexpr (OB == 2) {
@@ -94,68 +123,76 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, f32x4 (&acc)[RB][NT], 
     const int row_bytes = p.N * OB;
     const int cpr = (row_bytes + 15) / 16;  // 16-byte chunks per row
     const bool vec = (p.vec_c & 4) != 0;    // rows of C are 16-byte aligned and whole chunks
-    for (int q = lane; q < RB * 16 * cpr; q += 64) {
-        const int ml = q / cpr, c = q - ml * cpr;
-        const int m = base + ml;
-        if (m >= p.M) continue;
-        const char* src = stage + ml * pitch_o + c * 16;
-        char* dst = (char*)p.C + ((int64_t)m * p.ldc) * OB + c * 16;
-        if (vec) {
-            *(u32x4*)dst = *(const u32x4*)src;
-        } else {
-            for (int e = 0; e < 16 / OB; ++e)
-                if (c * 16 + e * OB < row_bytes) ((T*)dst)[e] = ((const T*)src)[e];
+    // chunk q = lane + 64 i of the RB*16 x cpr chunks is (row q / cpr, chunk
+    // q % cpr); stepped without a division per chunk
+    const int d_row = 64 / cpr, d_chunk = 64 - d_row * cpr;
+    int r = lane / cpr, c = lane - r * cpr;
+    while (r < RB * 16) {
+        const int mm = base + r;
+        if (mm < p.M) {
+            const char* src = stage + r * pitch_o + c * 16;
+            char* dst = (char*)p.C + ((int64_t)mm * p.ldc) * OB + c * 16;
+            if (vec) {
+                *(u32x4*)dst = *(const u32x4*)src;
+            } else {
+                for (int e = 0; e < 16 / OB; ++e)
+                    if (c * 16 + e * OB < row_bytes) ((T*)dst)[e] = ((const T*)src)[e];
+            }
+        }
+        r += d_row;
+        c += d_chunk;
+        if (c >= cpr) {
+            c -= cpr;
+            ++r;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
-// W^T into LDS ([n][k], rows n >= N zero-filled).
+// W^T into LDS ([n][k], rows n >= N zero-filled), by nth threads, one batch
+// (BT tasks per thread) at a time: load() brings a batch into registers,
+// store() writes it to LDS, so that other loads can be issued in between.
 // N x K W: a task is 8 consecutive k of one n, stored as one 16-byte LDS
 // write.  K x N W: a task is a pair of k-rows x 8 consecutive n (two 16-byte
 // loads), stored as eight 32-bit LDS writes of (k, k+1) pairs; consecutive
 // lanes take consecutive k-pairs, so the transposing writes of a wave fall
 // in consecutive dwords (a one-element-per-lane transpose put every lane of
-// a wave on the same bank).  Eight tasks per lane are loaded before any is
-// stored, so their latencies overlap.
+// a wave on the same bank).
 template <int DT, int NT, bool TRANS_B>
-__device__ inline void skinny_load_w(const SkinnyArgs& p, uint16_t* wt, int tid) {
-    constexpr int NP = NT * 16;
-    constexpr int NTH = SKINNY_WAVES * 64;
-    const bool vec_w = (p.vec_c & 2) != 0;  // W rows allow aligned 16-byte loads
-    if constexpr (TRANS_B) {
-        const int per_line = p.K / 8;
-        const int ntask = NP * per_line;
-        for (int t0 = 0; t0 < ntask; t0 += 8 * NTH) {
-            u32x4 v[8];
+struct WStage {
+    static constexpr int NP = NT * 16;
+    static constexpr int BT = TRANS_B ? 8 : 4;  // tasks per thread per batch: one batch at N = K = 160
+    u32x4 v0[BT], v1[BT];
+
+    __device__ static inline int ntask(const SkinnyArgs& p) {
+        return TRANS_B ? NP * (p.K / 8) : (p.K / 2) * (NP / 8);
+    }
+    // Task t of this workgroup is task (t + rot) mod ntask: every workgroup
+    // wants all of W at the same moment, and rotating the order spreads the
+    // requests over the cache channels.
+    __device__ static inline int rotated(int t, int rot, int nt_all) {
+        const int r = t + rot;
+        return r >= nt_all ? r - nt_all : r;
+    }
+    __device__ inline void load(const SkinnyArgs& p, int t0, int tid, int nth, int rot) {
+        const bool vec_w = (p.vec_c & 2) != 0;  // W rows allow aligned 16-byte loads
+        const int nt_all = ntask(p);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = t0 + i * NTH + tid;
-                v[i] = (u32x4){0, 0, 0, 0};
+        for (int i = 0; i < BT; ++i) {
+            const int tt = t0 + i * nth + tid;
+            v0[i] = v1[i] = (u32x4){0, 0, 0, 0};
+            if (tt >= nt_all) continue;
+            const int t = rotated(tt, rot, nt_all);
+            if constexpr (TRANS_B) {
+                const int per_line = p.K / 8;
                 const int n = t / per_line, k8 = (t - n * per_line) * 8;
-                if (t < ntask && n < p.N) {
-                    const int64_t idx = (int64_t)n * p.ldw + k8;
-                    v[i] = vec_w ? load16((const char*)p.W + idx * 2) : load_chunk_masked<DT>(p.W, idx, 8);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int t = t0 + i * NTH + tid;
-                const int n = t / per_line, k8 = (t - n * per_line) * 8;
-                if (t < ntask) *(u32x4*)(wt + n * p.pitch + k8) = v[i];
-            }
-        }
-    } else {
-        const int kp_count = p.K / 2;
-        const int ntask = kp_count * (NP / 8);
-        for (int t0 = 0; t0 < ntask; t0 += 4 * NTH) {
-            u32x4 v0[4], v1[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + i * NTH + tid;
-                v0[i] = v1[i] = (u32x4){0, 0, 0, 0};
+                if (n >= p.N) continue;
+                const int64_t idx = (int64_t)n * p.ldw + k8;
+                v0[i] = vec_w ? load16((const char*)p.W + idx * 2) : load_chunk_masked<DT>(p.W, idx, 8);
+            } else {
+                const int kp_count = p.K / 2;
                 const int n8 = (t / kp_count) * 8, kp = t - (t / kp_count) * kp_count;
-                if (t >= ntask || n8 >= p.N) continue;
+                if (n8 >= p.N) continue;
                 const int64_t i0 = (int64_t)(2 * kp) * p.ldw + n8, i1 = i0 + p.ldw;
                 if (vec_w && n8 + 8 <= p.N) {
                     v0[i] = load16((const char*)p.W + i0 * 2);
@@ -165,10 +202,22 @@ __device__ inline void skinny_load_w(const SkinnyArgs& p, uint16_t* wt, int tid)
                     v1[i] = load_chunk_masked<DT>(p.W, i1, p.N - n8);
                 }
             }
+        }
+    }
+    __device__ inline void store(const SkinnyArgs& p, uint16_t* wt, int t0, int tid, int nth,
+                                 int rot) const {
+        const int nt_all = ntask(p);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + i * NTH + tid;
-                if (t >= ntask) continue;
+        for (int i = 0; i < BT; ++i) {
+            const int tt = t0 + i * nth + tid;
+            if (tt >= nt_all) continue;
+            const int t = rotated(tt, rot, nt_all);
+            if constexpr (TRANS_B) {
+                const int per_line = p.K / 8;
+                const int n = t / per_line, k8 = (t - n * per_line) * 8;
+                *(u32x4*)(wt + n * p.pitch + k8) = v0[i];
+            } else {
+                const int kp_count = p.K / 2;
                 const int n8 = (t / kp_count) * 8, kp = t - (t / kp_count) * kp_count;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -179,49 +228,71 @@ __device__ inline void skinny_load_w(const SkinnyArgs& p, uint16_t* wt, int tid)
             }
         }
     }
-}
+};
 
-// The X operand registers of one wave's RB x 16 rows starting at row base.
-template <int RB>
-__device__ inline void skinny_load_x(const SkinnyArgs& p, int base, int lane,
-                                     u32x4 (&xf)[RB][SKINNY_KBMAX]) {
+// The X operand registers of k-blocks kb0 .. kb0 + KCH - 1 of one wave's
+// RB x 16 rows starting at row base.
+template <int RB, int KCH>
+__device__ inline void skinny_load_x(const SkinnyArgs& p, int base, int kb0, int lane,
+                                     u32x4 (&xf)[RB][KCH]) {
     const int KB = p.K / 32;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         int m = base + rb * 16 + (lane & 15);
         if (m >= p.M) m = p.M - 1;  // rows past the end: valid memory, never stored
-        const char* row = (const char*)p.X + ((int64_t)m * p.ldx + 8 * (lane >> 4)) * 2;
+        const char* row = (const char*)p.X + ((int64_t)m * p.ldx + 8 * (lane >> 4) + 32 * kb0) * 2;
 #pragma unroll
-        for (int kb = 0; kb < SKINNY_KBMAX; ++kb)
-            if (kb < KB) xf[rb][kb] = load16(row + kb * 64);
+        for (int kb = 0; kb < KCH; ++kb)
+            if (kb0 + kb < KB) xf[rb][kb] = load16(row + kb * 64);
     }
 }
 
-// Dynamic LDS: W^T (NT*16 rows x pitch elements), then one output staging
-// tile per wave (RB*16 rows x (NT*16*out_bytes + 16) bytes).
-__host__ __device__ inline size_t skinny_lds_bytes(int nt, int pitch, int out_bytes) {
-    return (size_t)nt * 16 * pitch * 2 +
-           (size_t)SKINNY_WAVES * skinny_rb(nt) * 16 * (nt * 16 * out_bytes + 16);
-}
-
 template <int DT, int NT, bool TRANS_B>
-__global__ __launch_bounds__(SKINNY_WAVES * 64, 2) void gemm_skinny_kernel(SkinnyArgs p) {
+__global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint16_t wt[];  // NT*16 rows x pitch
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int RB = skinny_rb(NT);
+    constexpr int KCH = skinny_kch(NT);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
     const int KB = p.K / 32;
-    const int rows_per_step = SKINNY_WAVES * RB * 16 * gridDim.x;
-    int base = (blockIdx.x * SKINNY_WAVES + wave) * RB * 16;
+    const int rows_per_step = nwaves * RB * 16 * gridDim.x;
+    int base = (blockIdx.x * nwaves + wave) * RB * 16;
 
-    // The first rows' X loads go out before W is staged, so the two overlap.
-    u32x4 xf[RB][SKINNY_KBMAX];
-    if (base < p.M) skinny_load_x(p, base, lane, xf);
-    skinny_load_w<DT, NT, TRANS_B>(p, wt, tid);
-    __syncthreads();
+    // Prologue: W and the bias are staged before any X is requested (issued
+    // together, X would flood the memory system and W, which every wave
+    // needs, would come back last: measured ~4.5 us instead of ~1-2 us), and
+    // the barrier that publishes W waits for LDS traffic only; then each
+    // wave requests its rows of X and starts its MFMAs as soon as they
+    // arrive, so later rows' loads overlap earlier rows' stores.
+    const int nth = blockDim.x;
+    WStage<DT, NT, TRANS_B> wst;
+    const int w_tasks = WStage<DT, NT, TRANS_B>::ntask(p);
+    const int rot = (int)(((int64_t)blockIdx.x * 97 * 64) % w_tasks);
+    wst.load(p, 0, tid, nth, rot);
+    uint32_t bias_bits[4];  // NT * 16 <= 256 values over at least 64 threads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = tid + i * nth;
+        bias_bits[i] = p.ep.epi != EPI_NONE && n < p.N ? load_elem_bits<DT>(p.ep.bias, n) : 0u;
+    }
+    wst.store(p, wt, 0, tid, nth, rot);
+    const int w_batch = WStage<DT, NT, TRANS_B>::BT * nth;
+    for (int t0 = w_batch; t0 < w_tasks; t0 += w_batch) {
+        wst.load(p, t0, tid, nth, rot);
+        wst.store(p, wt, t0, tid, nth, rot);
+    }
+    float* bias_s = (float*)(wt + NT * 16 * p.pitch);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (tid + i * nth < NT * 16) bias_s[tid + i * nth] = InType<DT>::to_f32(bias_bits[i]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    u32x4 xf[RB][KCH];
+    if (base < p.M) skinny_load_x<RB, KCH>(p, base, 0, lane, xf);
 
     const uint16_t* wrow = wt + (lane & 15) * p.pitch + 8 * (lane >> 4);
     const int ob = p.c_type == OUT_F32 ? 4 : 2;
-    char* stage = (char*)(wt + NT * 16 * p.pitch) + wave * (RB * 16 * (NT * 16 * ob + 16));
+    char* stage = (char*)(bias_s + NT * 16) + wave * skinny_stage_bytes(NT, ob);
     for (; base < p.M; base += rows_per_step) {
         f32x4 acc[RB][NT];
 #pragma unroll
@@ -229,23 +300,31 @@ __global__ __launch_bounds__(SKINNY_WAVES * 64, 2) void gemm_skinny_kernel(Skinn
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < SKINNY_KBMAX; ++kb) {
-            if (kb >= KB) break;
+        for (int c0 = 0; c0 < SKINNY_KBMAX; c0 += KCH) {
+            if (c0 >= KB) break;
+            if (c0 > 0) skinny_load_x<RB, KCH>(p, base, c0, lane, xf);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const u32x4 wf = *(const u32x4*)(wrow + nt * 16 * p.pitch + kb * 32);
+            for (int kb = 0; kb < KCH; ++kb) {
+                if (c0 + kb >= KB) break;
+                // all of this k-block's W^T fragments first, then the MFMAs
+                u32x4 wf[NT];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) mma_chunk<DT>(acc[rb][nt], wf, xf[rb][kb]);
+                for (int nt = 0; nt < NT; ++nt)
+                    wf[nt] = *(const u32x4*)(wrow + nt * 16 * p.pitch + (c0 + kb) * 32);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) mma_chunk<DT>(acc[rb][nt], wf[nt], xf[rb][kb]);
             }
         }
         // the next rows' loads overlap this epilogue's stores
-        if (base + rows_per_step < p.M) skinny_load_x(p, base + rows_per_step, lane, xf);
+        if (base + rows_per_step < p.M) skinny_load_x<RB, KCH>(p, base + rows_per_step, 0, lane, xf);
         if (p.c_type == OUT_F16)
-            skinny_finish<DT, OUT_F16, NT, RB>(p, acc, base, lane, stage);
+            skinny_finish<OUT_F16, NT, RB>(p, acc, bias_s, base, lane, stage);
         else if (p.c_type == OUT_BF16)
-            skinny_finish<DT, OUT_BF16, NT, RB>(p, acc, base, lane, stage);
+            skinny_finish<OUT_BF16, NT, RB>(p, acc, bias_s, base, lane, stage);
         else
-            skinny_finish<DT, OUT_F32, NT, RB>(p, acc, base, lane, stage);
+            skinny_finish<OUT_F32, NT, RB>(p, acc, bias_s, base, lane, stage);
     }
 }
 
