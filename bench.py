@@ -302,7 +302,7 @@ def main():
                      "traffic": traffic,
                      "kernel_us_mean": avg_kernel * 1e6,
                      "alg_bytes": gemm_alg_bytes(M, N, K, 2, 2),
-                     "kernel": "gemm_direct_kernel<fp16, 256x256 tile, 8 waves, K x N B>"},
+                     "kernel": "gemm_direct_kernel<fp16, 256x256 tile, 8 waves, 16x16x32 MFMA, K x N B>"},
     }
     if not args.no_extra:
         extra_steps = max(10, min(args.steps, 30))
