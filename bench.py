@@ -137,7 +137,8 @@ def _med(x):
 
 
 def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
-    """Per shape: dequant (HBM-cold by rotating weight sets), GEMM, tok/s."""
+    """Per shape: dequant (HBM-cold by rotating weight sets), GEMM, the fused
+    q4 GEMM (gemm_q4_f16), tok/s."""
     out = {}
     for shape in ("up", "attn", "down"):
         A, q, N, K = inputs.prefill_projection(shape)
@@ -158,21 +159,30 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
         def gem():
             dge.gemm_f16(dA, ws[0], C, trans_b=True, workspace=work)
 
+        def fused():
+            i = it[0] % nset
+            it[0] += 1
+            dge.gemm_q4_f16(dA, qs[i], N, K, C, workspace=work)
+
         td, _ = time_launches(deq, steps, 3, torch)
         tg, _ = time_launches(gem, steps, 3, torch)
+        tf, _ = time_launches(fused, steps, 3, torch)
         out[shape] = {"N": N, "K": K, "dequant_us": td * 1e6, "gemm_us": tg * 1e6,
                       "dequant_GBs": dequant_alg_bytes(N, K) / td / 1e9,
                       "dequant_hbm_frac": dequant_alg_bytes(N, K) / td / 1e9 / HBM_PEAK_GBS,
                       "gemm_TFLOPs": gemm_flops(2048, N, K) / tg / 1e12,
                       "gemm_mfma_frac": gemm_flops(2048, N, K) / tg / 1e12 / PEAK["f16"],
                       "tok_s_dequant_per_call": 2048 / (td + tg),
-                      "tok_s_gemm_only": 2048 / tg}
+                      "tok_s_gemm_only": 2048 / tg,
+                      "fused_us": tf * 1e6, "tok_s_fused": 2048 / tf}
         del qs, ws, C, work, dA
     t = {k: (out[k]["dequant_us"] + out[k]["gemm_us"]) * 1e-6 for k in out}
     g = {k: out[k]["gemm_us"] * 1e-6 for k in out}
+    f = {k: out[k]["fused_us"] * 1e-6 for k in out}
     out["stack_7b_like"] = {
         "tok_s_dequant_per_call": prefill_stack_tokens_per_s(t["attn"], t["up"], t["down"]),
-        "tok_s_gemm_only": prefill_stack_tokens_per_s(g["attn"], g["up"], g["down"])}
+        "tok_s_gemm_only": prefill_stack_tokens_per_s(g["attn"], g["up"], g["down"]),
+        "tok_s_fused": prefill_stack_tokens_per_s(f["attn"], f["up"], f["down"])}
     return out
 
 

@@ -23,6 +23,7 @@ TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x2
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "dequant_q4_f16", "prefill_q4_f16",
+           "gemm_q4_f16",
            "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_status_string", "gemm_init")
 
 
@@ -62,6 +63,9 @@ def lib():
         L.prefill_q4_f16.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, i32, i32, vp, vp, sz,
                                      vp]
         L.prefill_q4_f16.restype = i32
+        L.gemm_q4_f16.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, i32, i32, vp, vp, sz,
+                                  ctypes.POINTER(Tuning), vp]
+        L.gemm_q4_f16.restype = i32
         L.gemm_workspace_size.argtypes = [i64, i64, i64, i32]
         L.gemm_workspace_size.restype = sz
         L.gemm_workspace_size_splits.argtypes = [i64, i64, i32]
@@ -189,6 +193,21 @@ def prefill_q4_f16(A, q, N, K, w16=None, C=None, *, out_dtype=torch.float16, epi
     _check(lib().prefill_q4_f16(M, N, K, _ptr(A), _ld(A, "A"), _ptr(q), _ptr(w16), _ptr(C),
                                 _ld(C, "C"), OUT[C.dtype], EPI[epi], _ptr(bias), _ptr(workspace),
                                 ws_bytes, _stream(stream)), "prefill_q4_f16")
+    return C
+
+
+def gemm_q4_f16(A, q, N, K, C=None, *, out_dtype=torch.float16, epi="none", bias=None,
+                workspace=None, algo="auto", tile="auto", splits=0, stream=None):
+    """C = epi(A @ dequant(q)^T) with the dequantisation fused into the GEMM
+    (algo="mfma_direct" requires the fused kernel)."""
+    M = A.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    t = Tuning(ALGO[algo], TILE[tile], int(splits))
+    _check(lib().gemm_q4_f16(M, N, K, _ptr(A), _ld(A, "A"), _ptr(q), _ptr(C), _ld(C, "C"),
+                             OUT[C.dtype], EPI[epi], _ptr(bias), _ptr(workspace), ws_bytes,
+                             ctypes.byref(t), _stream(stream)), "gemm_q4_f16")
     return C
 
 

@@ -90,6 +90,7 @@ struct Gemm {
     void* ws;
     size_t ws_bytes;
     hipStream_t stream;
+    int b_q4;  // B is an N x K weight as q4 blocks (18 bytes per 32 weights)
 };
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
@@ -117,9 +118,10 @@ gemm_status_t validate(const Gemm& g) {
     if (g.epi != EPI_NONE && !g.bias) return GEMM_ERR_INVALID_VALUE;
     const Range rc = span(g.C, g.M, g.N, g.ldc, out_bytes(g.c_type));
     const Range ra = g.K > 0 ? span(g.A, g.M, g.K, g.lda, in_bytes(g.dt)) : Range{0, 0};
-    const Range rb = g.K > 0 ? (g.trans_b ? span(g.B, g.N, g.K, g.ldb, in_bytes(g.dt))
-                                          : span(g.B, g.K, g.N, g.ldb, in_bytes(g.dt)))
-                             : Range{0, 0};
+    const Range rb = g.K <= 0 ? Range{0, 0}
+                     : g.b_q4 ? Range{(uintptr_t)g.B, (uintptr_t)g.B + (uintptr_t)(g.N * (g.K / 32) * 18)}
+                     : g.trans_b ? span(g.B, g.N, g.K, g.ldb, in_bytes(g.dt))
+                                 : span(g.B, g.K, g.N, g.ldb, in_bytes(g.dt));
     const Range rbias = g.epi != EPI_NONE ? span(g.bias, 1, g.N, g.N, in_bytes(g.dt)) : Range{0, 0};
     if (overlaps(rc, ra) || overlaps(rc, rb) || overlaps(rc, rbias)) return GEMM_ERR_INVALID_VALUE;
     return GEMM_OK;
@@ -211,16 +213,18 @@ double schedule_us(int64_t M, int64_t N, int64_t K, int tile, int splits, int bk
 }
 
 // Joint choice of tile shape and K split.  tile / splits: the caller's
-// request (GEMM_TILE_AUTO / 0 = free).  A split is only considered while
-// ws_bytes covers its partials; each K slice keeps at least 16 stages.
+// request (GEMM_TILE_AUTO / 0 = free); allowed: bit t set for each tile id
+// that may be chosen.  A split is only considered while ws_bytes covers its
+// partials; each K slice keeps at least 16 stages.
 void choose_schedule(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
-                     int* tile, int* splits) {
+                     int* tile, int* splits, unsigned allowed = ~0u) {
     const int bk = stage_k(dt);
     const int t_lo = *tile == GEMM_TILE_AUTO ? TILE_256x256 : *tile;
     const int t_hi = *tile == GEMM_TILE_AUTO ? TILE_LAST : *tile;
     int best_t = t_lo, best_s = 1;
     double best = 1e300;
     for (int t = t_lo; t <= t_hi; ++t) {
+        if (!(allowed >> t & 1u)) continue;
         for (int sp = 1; sp <= 8; ++sp) {
             if (*splits > 0 && sp != *splits) continue;
             if (sp > 1 && (K / sp < 16 * (int64_t)bk || ws_bytes < ws_bytes_for(M, N, sp)))
@@ -252,8 +256,22 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
     if (tile != GEMM_TILE_AUTO && (tile < TILE_256x256 || tile > TILE_LAST))
         return GEMM_ERR_INVALID_VALUE;
     const bool explicit_split = splits > 1;
+    unsigned allowed = ~0u;
+    if (g.b_q4) {
+        // the fused q4 kernel takes full tiles, whole 64-deep stages, a 4-byte
+        // aligned block array and the direct-load alignment of A and C
+        allowed = 0;
+        for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
+            const TileShape s = tile_shape(t);
+            if (g.M % s.bm == 0 && g.N % s.bn == 0) allowed |= 1u << t;
+        }
+        if (tile != GEMM_TILE_AUTO) allowed &= 1u << tile;
+        const bool ok = allowed && g.K % 64 == 0 && ((uintptr_t)g.B & 3) == 0 && aligned16(g.A) &&
+                        aligned16(g.C) && g.lda % 8 == 0 && (g.ldc * out_bytes(g.c_type)) % 16 == 0;
+        if (!ok) return GEMM_ERR_NOT_SUPPORTED;
+    }
     if (tile == GEMM_TILE_AUTO || splits == 0)
-        choose_schedule(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, &tile, &splits);
+        choose_schedule(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, &tile, &splits, allowed);
     const TileShape ts = tile_shape(tile);
     const int bk = stage_k(g.dt);
     const int max_splits = std::max(1, ceil_div(g.K, bk));
@@ -290,8 +308,9 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
     a.group_m = std::max(1, std::min(env_int("GEMM_GROUP_M", gm), a.tiles_m));
     a.c_type = g.c_type;
     const int vec_el = 16 / in_bytes(g.dt);
-    const bool vec = aligned16(g.A) && aligned16(g.B) && aligned16(g.C) && g.lda % vec_el == 0 &&
-                     g.ldb % vec_el == 0 && (g.ldc * out_bytes(g.c_type)) % 16 == 0;
+    const bool vec = aligned16(g.A) && (g.b_q4 || aligned16(g.B)) && aligned16(g.C) &&
+                     g.lda % vec_el == 0 && (g.b_q4 || g.ldb % vec_el == 0) &&
+                     (g.ldc * out_bytes(g.c_type)) % 16 == 0;
     a.vec_ok = vec ? 1 : 0;
     a.ep = make_epilogue(g);
     const bool fast = vec && g.M % ts.bm == 0 && g.N % ts.bn == 0 && g.K % bk == 0 &&
@@ -299,6 +318,13 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
     const int64_t nwg = (int64_t)a.tiles_m * a.tiles_n * splits;
     if (nwg > 0x7fffffff) return GEMM_ERR_NOT_SUPPORTED;
     hipError_t e;
+    if (g.b_q4) {
+        if (!fast) return GEMM_ERR_NOT_SUPPORTED;
+        e = launch_mfma_q4_f16(tile, a, (int)nwg, g.stream);
+        if (e == hipSuccess && splits > 1)
+            e = launch_splitk_fixup(g.dt, simple_args(g), (const float*)g.ws, splits, g.stream);
+        return launch_status(e);
+    }
     const bool use_direct = direct && fast && g.dt != IN_F32 &&
                             (g.trans_b || ts.bn >= 128) && env_int("GEMM_DIRECT", 1) != 0;
     if (use_direct) {
@@ -414,6 +440,7 @@ Gemm make_gemm(int dt, int64_t M, int64_t N, int64_t K, float alpha, const void*
     g.ws = workspace;
     g.ws_bytes = workspace_bytes;
     g.stream = (hipStream_t)stream;
+    g.b_q4 = 0;
     return g;
 }
 
@@ -498,6 +525,55 @@ gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int
         if (st != GEMM_OK) return st;
     }
     return run_gemm(g, nullptr);
+}
+
+gemm_status_t gemm_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                          const void* q, void* C, int64_t ldc, gemm_out_t c_type,
+                          gemm_epilogue_t epi, const void* bias, void* workspace,
+                          size_t workspace_bytes, const gemm_tuning_t* tuning, void* stream) {
+    gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
+    if (tuning) tn = *tuning;
+    if ((tn.algo != GEMM_ALGO_AUTO && tn.algo != GEMM_ALGO_MFMA_DIRECT) ||
+        tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8 || tn.splits < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return GEMM_ERR_INVALID_VALUE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (K > 0 && (!q || ((uintptr_t)q & 1) != 0)) return GEMM_ERR_INVALID_VALUE;
+    Gemm g = make_gemm(IN_F16, M, N, K, 1.0f, A, lda, q, std::max<int64_t>(K, 1), 1, 0.0f, C, ldc,
+                       c_type, epi, bias, workspace, workspace_bytes, stream);
+    g.b_q4 = 1;
+    gemm_status_t st = validate(g);
+    if (st != GEMM_OK) return st;
+    if ((st = forced_failure()) != GEMM_OK) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    if (K > 0) {
+        st = run_mfma(g, tn.tile, tn.splits, dev.cus, 1);
+        if (st != GEMM_ERR_NOT_SUPPORTED) return st;
+        if (tn.algo == GEMM_ALGO_MFMA_DIRECT) return st;  // the fused kernel was required
+    }
+    // Shapes the fused kernel does not take: expand the weights into the
+    // workspace (N x K fp16) and run the two-pass path.
+    const size_t need = (size_t)N * (size_t)K * 2;
+    if (K > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return GEMM_ERR_WORKSPACE;
+    g.b_q4 = 0;
+    if (K > 0) {
+        const Range rw = span(workspace, N, K, K, 2);
+        const Range rq = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(N * (K / 32) * 18)};
+        if (overlaps(rw, rq) || overlaps(rw, span(A, M, K, lda, 2)) ||
+            overlaps(rw, span(C, M, N, ldc, out_bytes((int)c_type))))
+            return GEMM_ERR_INVALID_VALUE;
+        st = dequant_q4_f16(q, workspace, N, K, K, stream);
+        if (st != GEMM_OK) return st;
+        g.B = workspace;
+        g.ldb = K;
+    }
+    g.ws = nullptr;
+    g.ws_bytes = 0;
+    gemm_tuning_t two_pass{GEMM_ALGO_AUTO, tn.tile, tn.splits > 1 ? 1 : 0};
+    return run_gemm(g, &two_pass);
 }
 
 size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {

@@ -46,6 +46,9 @@ hipError_t launch_mfma_f32(int tile, int trans_b, int fast, const MfmaArgs& a, i
 hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, hipStream_t s);
 hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg,
                                    hipStream_t s);
+// Fused q4-weight GEMM (p.B = q4 blocks of an N x K weight, 4-byte aligned;
+// K % 64 == 0; full tiles of the given shape only).
+hipError_t launch_mfma_q4_f16(int tile, const MfmaArgs& a, int nwg, hipStream_t s);
 
 // Tall-skinny kernel: nt = 16-column tiles of N (even, 2..16), waves per
 // workgroup (1..16), lds = dynamic LDS bytes (skinny_lds_bytes).

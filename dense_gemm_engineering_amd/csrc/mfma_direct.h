@@ -35,6 +35,19 @@
 //    8 consecutive k one operand register quad holds.  The 16-byte chunks of
 //    k-row k are XOR-swizzled (swz_b<MS>) so that the k-rows and columns
 //    the lane groups of one read cover fall in different bank groups.
+//  * Fused q4 weights (Q4 = true, N x K weights as 18-byte blocks: a binary16
+//    scale d, then 16 code bytes, byte i holding element i in its low nibble
+//    and element i + 16 in its high nibble, value d (q - 8); "02 · 8m/8m② —
+//    Tiled wmma f16 prefill GEMM" §3.2): the B tile is not copied but made.
+//    After the barrier that frees a buffer, each thread loads the 20
+//    4-byte-aligned bytes holding one 32-weight block of the stage two ahead
+//    into registers; before the next barrier it decodes them and writes four
+//    16-byte rows chunks into the swizzled k-contiguous B layout.  Decoding
+//    uses packed binary16 arithmetic: (0x6400 | q) is 1024 + q exactly,
+//    minus 1032 gives q - 8 exactly, and one packed multiply by d rounds
+//    d (q - 8) once to nearest-even, the value the two-pass path stores.
+//    The fp16 weight matrix is never written (the dequant pass and its
+//    re-read, 90 of the 115.5 MB a 11008 x 4096 projection moves, go away).
 //  * Software pipeline, one barrier per stage: the fragment reads of the
 //    next k-block are interleaved with the MFMAs of the current one (the LDS
 //    counter can track 15 outstanding reads, so they are issued a few at a
@@ -102,6 +115,19 @@ __device__ inline void interleave_reads() {
     }
 }
 
+// Scheduling pattern for NM MFMAs interleaved with VALU work: after each
+// MFMA up to V VALU instructions, and NW LDS writes spread evenly.
+template <int NM, int V, int NW, int R = 0>
+__device__ inline void interleave_valu() {
+    if constexpr (R < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // V VALU
+        constexpr int w = (R + 1) * NW / NM - R * NW / NM;
+        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);  // LDS writes
+        interleave_valu<NM, V, NW, R + 1>();
+    }
+}
+
 template <int DT>
 __device__ inline void mma32(f32x16& acc, const u32x4& a, const u32x4& b) {
     if constexpr (DT == IN_F16)
@@ -116,10 +142,26 @@ template <int MS> struct AccBlock;
 template <> struct AccBlock<16> { typedef f32x4 T; };
 template <> struct AccBlock<32> { typedef f32x16 T; };
 
-template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS>
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// Eight q4 codes (nib: the low or high nibbles of 4 code bytes, one per
+// byte) as eight binary16 weights d * (q - 8), packed in pairs: v_perm_b32
+// puts byte 0x64 above each code, giving 1024 + q exactly, minus 1032 is
+// q - 8 exactly, and one packed multiply by d rounds once.
+__device__ inline void q4_decode4(uint32_t nib, h2v d2, uint32_t* o) {
+    const h2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    // selector bytes: 0-3 pick bytes of nib, 4-7 bytes of 0x64646464
+    const uint32_t v01 = __builtin_amdgcn_perm(0x64646464u, nib, 0x04010400u);  // q0, q1
+    const uint32_t v23 = __builtin_amdgcn_perm(0x64646464u, nib, 0x04030402u);  // q2, q3
+    o[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2v, v01) - off) * d2);
+    o[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2v, v23) - off) * d2);
+}
+
+template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS, bool Q4 = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p) {
     static_assert(DT == IN_F16 || DT == IN_BF16, "16-bit inputs only");
     static_assert(MS == 16 || MS == 32, "MFMA block size");
+    static_assert(!Q4 || (TRANS_B && DT == IN_F16), "q4 weights are N x K, with fp16 A");
     constexpr int NW = WM * WN;
     constexpr int BK = 64;
     constexpr int KBLK = 512 / MS;   // k per k-block: 32 (16x16x32) or 16 (32x32x16)
@@ -130,8 +172,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int TM = WTM / MS, TN = WTN / MS;
     static_assert(TM * MS == WTM && TN * MS == WTN, "wave tile must be a multiple of the block");
     constexpr int IA = A_BYTES / 1024 / NW;  // direct-load instructions per wave per stage
-    constexpr int IB = B_BYTES / 1024 / NW;
-    static_assert(IA * 1024 * NW == A_BYTES && IB * 1024 * NW == B_BYTES, "stage split");
+    constexpr int IB = Q4 ? 0 : B_BYTES / 1024 / NW;
+    static_assert(IA * 1024 * NW == A_BYTES && (Q4 || IB * 1024 * NW == B_BYTES), "stage split");
     static_assert(TRANS_B || BN >= 128, "transposed-read layout needs 16+ chunks per k-row");
     constexpr int CPR_B = BN / 8;             // 16-byte chunks per k-row of a K x N B tile
     constexpr int RPI_B = 1024 / (BN * 2);    // k-rows per 1 KB direct-load instruction
@@ -200,6 +242,53 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             } else {
                 const int chunk = b_lane_chunk ^ swz_b<MS>(b_krow0 + RPI_B * i);
                 lds_dma16(gb + i * b_step + chunk * 8, lb + i * 1024);
+            }
+        }
+    };
+
+    // ---- q4 B producer: task t = (tile row t / 2, block t % 2 of the stage)
+    constexpr int NTHR = NW * 64;
+    constexpr int QT = Q4 ? (2 * BN + NTHR - 1) / NTHR : 1;  // tasks per thread per stage
+    static_assert(!Q4 || (2 * BN) % NTHR == 0 || 2 * BN < NTHR, "q4 task split");
+    uint32_t qraw[QT][5];
+    const int64_t qnb = p.K / 32;  // blocks per weight row (even: K % 64 == 0)
+    auto q4_load = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+            const int t = tid + i * NTHR;
+            if ((2 * BN) % NTHR != 0 && t >= 2 * BN) continue;  // folds away when tasks divide evenly
+            const int row = t >> 1, j = t & 1;
+            // block (n0 + row, kbeg / 32 + 2 kt + j) sits at 18 x its index; the
+            // index of j = 0 is even, so that block starts 4-byte aligned and
+            // j = 1 starts 2 bytes past the 16th byte: both read 20 aligned bytes
+            const int64_t blk = (int64_t)(n0 + row) * qnb + kbeg / 32 + 2 * kt;
+            const uint32_t* src = (const uint32_t*)((const uint8_t*)p.B + 18 * blk + 16 * j);
+#pragma unroll
+            for (int e = 0; e < 5; ++e) qraw[i][e] = src[e];
+        }
+    };
+    auto q4_store = [&](int st) {
+        DGE_LDS char* lb = (DGE_LDS char*)&lds[st][A_BYTES];
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+            const int t = tid + i * NTHR;
+            if ((2 * BN) % NTHR != 0 && t >= 2 * BN) continue;  // folds away when tasks divide evenly
+            const int row = t >> 1, j = t & 1;
+            const uint32_t* w = qraw[i];
+            const uint16_t dbits = (uint16_t)(j ? (w[0] >> 16) : (w[0] & 0xFFFFu));
+            const _Float16 d = __builtin_bit_cast(_Float16, dbits);
+            const h2v d2 = {d, d};
+            uint32_t c[4];  // the 16 code bytes
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[e] = j ? w[e + 1] : (w[e] >> 16) | (w[e + 1] << 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // chunk q: elements 8q .. 8q + 7 of the block
+                const int shift = q < 2 ? 0 : 4, base = (q & 1) * 2;
+                uint32_t o[4];
+                q4_decode4((c[base] >> shift) & 0x0F0F0F0Fu, d2, o);
+                q4_decode4((c[base + 1] >> shift) & 0x0F0F0F0Fu, d2, o + 2);
+                *(DGE_LDS u32x4*)(lb + row * 128 + (((4 * j + q) ^ swz_k<MS>(row)) << 4)) =
+                    (u32x4){o[0], o[1], o[2], o[3]};
             }
         }
     };
@@ -277,15 +366,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // k-blocks.  Issued as one burst they stall the wave's MFMA issue while
     // the address unit works through them (measured: ~2960 -> ~2680 cycles
     // per stage for the 8-wave tile).
-    constexpr int DPART = KB - 1 < 3 ? KB - 1 : 3;  // 1 (all after the barrier) for MS = 16
+    // 1 (all after the barrier) for MS = 16 and for q4 (whose decode waits
+    // for all outstanding loads and must not meet fresh ones)
+    constexpr int DPART = Q4 ? 1 : (KB - 1 < 3 ? KB - 1 : 3);
     constexpr int NP0 = NDMA / DPART;                    // loads in the first part
     constexpr int TAIL = NMF / (MS == 16 ? 4 : 2) > 0 ? NMF / (MS == 16 ? 4 : 2) : 1;  // after the barrier
 
     // Prologue: stages 0 and 1 in flight, wait for stage 0, read its k-block 0.
     issue_part(0, 0, 0, NDMA);
+    if constexpr (Q4) q4_load(0);
     issue_part(1, nk > 1 ? 1 : 0, 0, NP0);
+    if constexpr (Q4) q4_store(0);
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((NP0 & 15) | ((NP0 >> 4) << 14)));  // vmcnt(NP0)
     __syncthreads();
+    if constexpr (Q4) q4_load(nk > 1 ? 1 : 0);
     read_kblock(0, 0, fa[0], fb[0]);
 
     // Steady state, stage kt (buffer kt & 1), k-blocks 0 .. KB-1 with their
@@ -312,7 +406,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         }
         constexpr int L = (KB - 1) & 1;
         mma_range(fa[L], fb[L], 0, NMF - TAIL);
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - TAIL, 0);
+        if constexpr (Q4) {
+            // q4: stage kt + 1's B tile (buffer kt + 1 & 1, free since the last
+            // barrier), from the blocks loaded a stage ago, decoded between
+            // this k-block's MFMAs: each MFMA is followed by a share of the
+            // decode's VALU work and, now and then, one of its LDS writes
+            q4_store(st ^ 1);
+            interleave_valu<NMF - TAIL, (QT * 72 + NMF - TAIL - 1) / (NMF - TAIL), QT * 4>();
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - TAIL, 0);
+        }
         // nothing moves across the barrier (the MFMAs above would otherwise
         // drift past it, leaving the matrix unit idle while the wave waits)
         __builtin_amdgcn_sched_barrier(0);
@@ -321,6 +424,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         __syncthreads();
 
         issue_part(st, min(kt + 2, nk - 1), 0, NP0);
+        if constexpr (Q4) q4_load(min(kt + 2, nk - 1));
         read_kblock(st ^ 1, 0, fa[0], fb[0]);
         mma_range(fa[L], fb[L], NMF - TAIL, NMF);
 #pragma unroll

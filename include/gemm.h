@@ -17,6 +17,11 @@
  *     the prefill projection of the same page: dequantise an N x K q4 weight
  *     into a caller-supplied binary16 scratch, then C = A * W^T on the same
  *     stream (§1 route 2, §3.2 host routing).
+ *   gemm_q4_f16:
+ *     the same projection with the dequantisation fused into the GEMM's
+ *     B-tile producer, so the binary16 weight is never written to memory:
+ *     the dequant-in-GEMM successor that §2.3 of the same page names for
+ *     the three-pass cost of the dequant-then-GEMM route.
  *
  * Conventions (all entry points)
  *   - Row-major throughout; leading dimensions are in elements.
@@ -163,6 +168,28 @@ gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int
                              const void* q, void* w16, void* C, int64_t ldc, gemm_out_t c_type,
                              gemm_epilogue_t epi, const void* bias, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Fused prefill projection: C = epi(A * dequant(q)^T), A M x K fp16 (lda),
+ * q the N x K weight as q4 blocks (layout of dequant_q4_f16, 2-byte aligned),
+ * C M x N (ldc, c_type), alpha = 1, beta = 0, bias as for gemm_f16.  K % 32
+ * == 0 is required (GEMM_ERR_INVALID_VALUE otherwise).  The weights are
+ * decoded inside the GEMM kernel with one RNE rounding of d * (code - 8), the
+ * same binary16 values dequant_q4_f16 writes, so the result equals
+ * prefill_q4_f16's up to the GEMM's own summation order.  The fused kernel
+ * takes shapes whose M and N are multiples of a 128 x 64 (or larger) tile,
+ * K % 64 == 0, q 4-byte aligned and A, C 16-byte aligned with lda % 8 == 0;
+ * the workspace then only serves a K split (gemm_workspace_size with
+ * GEMM_IN_F16 gives its size; less workspace = no split).  Any other shape
+ * expands the weights into the workspace first, which must then hold
+ * 2 * N * K bytes, 16-byte aligned (GEMM_ERR_WORKSPACE otherwise).
+ * tuning (may be NULL): algo GEMM_ALGO_AUTO or GEMM_ALGO_MFMA_DIRECT (= the
+ * fused kernel is required: GEMM_ERR_NOT_SUPPORTED for a shape it cannot
+ * take), tile and splits as for gemm_ex; other algos are
+ * GEMM_ERR_INVALID_VALUE. */
+gemm_status_t gemm_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                          const void* q, void* C, int64_t ldc, gemm_out_t c_type,
+                          gemm_epilogue_t epi, const void* bias, void* workspace,
+                          size_t workspace_bytes, const gemm_tuning_t* tuning, void* stream);
 
 /* Workspace bytes the automatic schedule of this shape would use (0 if it
  * would not split K).  dtype is a gemm_in_t. */

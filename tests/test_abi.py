@@ -82,6 +82,21 @@ def test_prefill_validation():
                             None) == 1
 
 
+def test_fused_q4_validation():
+    L = dge.lib()
+    # K not a multiple of 32; odd q address; bad tuning algo
+    assert L.gemm_q4_f16(4, 4, 40, 8, 40, 4096, 1 << 24, 4, 1, 0, None, None, 0, None,
+                         None) == 1
+    assert L.gemm_q4_f16(4, 4, 64, 8, 64, 4097, 1 << 24, 4, 1, 0, None, None, 0, None,
+                         None) == 1
+    t = dge.Tuning(dge.ALGO["naive"], 0, 0)
+    assert L.gemm_q4_f16(4, 4, 64, 8, 64, 4096, 1 << 24, 4, 1, 0, None, None, 0,
+                         ctypes.byref(t), None) == 1
+    # empty problem
+    assert L.gemm_q4_f16(0, 4, 64, 8, 64, 4096, 1 << 24, 4, 1, 0, None, None, 0, None,
+                         None) == 0
+
+
 def test_workspace_sizes():
     assert dge.gemm_workspace_size_splits(100, 50, 1) == 0
     assert dge.gemm_workspace_size_splits(100, 50, 3) == 3 * 100 * 50 * 4
