@@ -186,6 +186,33 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
     return out
 
 
+def bench_decode(dge, inputs, torch, steps, rotate_bytes=300e6):
+    """The decode shape: M input rows against one 4096 x 4096 fp16 weight
+    (HBM-cold by rotating weight copies); bound by reading W once."""
+    out = {}
+    N = K = 4096
+    _, W = inputs.decode_shape(1)
+    nset = max(1, int(np.ceil(rotate_bytes / (N * K * 2))))
+    Ws = [_dev(W, "f16", torch) for _ in range(nset)]
+    for M in inputs.DECODE_ROWS:
+        X, _ = inputs.decode_shape(M)
+        dX = _dev(X, "f16", torch)
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        it = [0]
+
+        def run():
+            i = it[0] % nset
+            it[0] += 1
+            dge.gemm_f16(dX, Ws[i], C, trans_b=True)
+
+        t, _ = time_launches(run, steps, 3, torch)
+        alg = gemm_alg_bytes(M, N, K, 2, 2)
+        out["M%d" % M] = {"us": t * 1e6, "GBs": alg / t / 1e9, "hbm_frac": alg / t / 1e9 / HBM_PEAK_GBS,
+                          "tokens_per_s": M / t}
+    del Ws
+    return out
+
+
 def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
     out = {}
     for N in (160, 32):
@@ -318,6 +345,7 @@ def main():
         extra_steps = max(10, min(args.steps, 30))
         line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps)
         line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps)
+        line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps)
         line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)

@@ -18,7 +18,8 @@ STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_NOT_SUPP
 EPI = {"none": 0, "bias": 1, "bias_gelu": 2}
 OUT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 IN = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
-ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "mfma": 3, "mfma_direct": 4, "skinny": 5}
+ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "mfma": 3, "mfma_direct": 4, "skinny": 5,
+        "decode": 6}
 TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x256w8": 5}
 
 # Every symbol include/gemm.h declares.

@@ -381,12 +381,34 @@ gemm_status_t run_skinny(const Gemm& g, int cus) {
     return launch_status(launch_skinny(g.dt, nt, g.trans_b, a, grid, waves, lds, g.stream));
 }
 
+// The decode-shaped kernel: a few rows of 16-bit X against an N x K weight.
+bool decode_eligible(const Gemm& g) {
+    return g.dt != IN_F32 && g.trans_b == 1 && !g.b_q4 && g.M >= 1 && g.M <= 64 &&
+           g.K % 8 == 0 && aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0;
+}
+
+gemm_status_t run_decode(const Gemm& g) {
+    DecodeArgs a;
+    a.X = g.A;
+    a.W = g.B;
+    a.C = g.C;
+    a.ldx = g.lda;
+    a.ldw = g.ldb;
+    a.ldc = g.ldc;
+    a.M = (int)g.M;
+    a.N = (int)g.N;
+    a.K = (int)g.K;
+    a.c_type = g.c_type;
+    a.ep = make_epilogue(g);
+    return launch_status(launch_decode(g.dt, a, g.stream));
+}
+
 gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
     gemm_status_t st = validate(g);
     if (st != GEMM_OK) return st;
     gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
     if (tuning) tn = *tuning;
-    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_SKINNY) return GEMM_ERR_INVALID_VALUE;
+    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_DECODE) return GEMM_ERR_INVALID_VALUE;
     if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8) return GEMM_ERR_INVALID_VALUE;
     if (tn.splits < 0) return GEMM_ERR_INVALID_VALUE;
     if (g.M == 0 || g.N == 0) return GEMM_OK;
@@ -406,7 +428,13 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
             if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
             if (skinny_eligible(g)) return run_skinny(g, dev.cus);
             return run_mfma(g, tn.tile, 1, dev.cus, 1);
+        case GEMM_ALGO_DECODE:
+            if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
+            if (g.K > 0 && decode_eligible(g)) return run_decode(g);
+            return run_mfma(g, tn.tile, 1, dev.cus, 1);
         case GEMM_ALGO_AUTO:
+            if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && g.K > 0 && decode_eligible(g))
+                return run_decode(g);
             if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && skinny_eligible(g) &&
                 g.M >= 8 * g.N && g.M >= 4096 && env_int("GEMM_SKINNY", 1) != 0)
                 return run_skinny(g, dev.cus);

@@ -1,0 +1,114 @@
+// Decode-shaped GEMM: C = epi(alpha X W^T + beta C) for a few input rows
+// (M <= 64) against an N x K weight ("Matrix Multiplication: The Operation
+// Behind Modern AI", "The shape a language model actually runs": at M = 1
+// the best possible intensity is ~1 FLOP per byte, so the time is the time
+// to read W once).  Everything is arranged around streaming W from HBM:
+//
+//  * A workgroup owns 16 weight rows and all M input rows; its 8 waves split
+//    K into 8 slices of whole 32-deep k-blocks.  Within a wave, the MFMA "A"
+//    operand is 8 consecutive k of one weight row per lane, i.e. a 16-byte
+//    load straight from W into registers (no LDS), and the "B" operand is 8
+//    consecutive k of one row of X (L2-resident: X is at most 64 x K).  The
+//    product is C^T = W X^T in 16 x 16 blocks, MT = ceil(M / 16) of them.
+//  * Loads for 16 k-blocks (8 for M > 32) are issued before their MFMAs, so
+//    each lane keeps up to 256 bytes of W (and of X) in flight; with 8 waves
+//    per CU that is ~128 KB of W per CU, and a 4096-deep K costs each wave a
+//    single round trip to memory.
+//  * The 8 partial blocks are summed through LDS in a fixed order (slice 0
+//    first), so results do not depend on timing, and the fused epilogue
+//    writes 16 consecutive columns per output row.
+#pragma once
+
+#include "device_common.h"
+#include "mfma_gemm.h"
+
+namespace dge {
+
+struct DecodeArgs {
+    const void* X;  // M x K, row-major
+    const void* W;  // N x K, row-major
+    void* C;        // M x N
+    int64_t ldx, ldw, ldc;
+    int M, N, K;
+    int c_type;
+    Epilogue ep;
+};
+
+constexpr int DECODE_WAVES = 8;
+// k-blocks whose loads are issued together: 16 (a 4096-deep K in one round
+// trip per wave) while the registers allow, 8 for M > 32
+__host__ __device__ constexpr int decode_batch(int mt) { return mt <= 2 ? 16 : 8; }
+
+template <int DT, int MT>
+__global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeArgs p) {
+    // partial C^T blocks of every wave: [wave][mt][16 n][16 m] fp32
+    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][MT][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int nkb = (p.K + 31) / 32;
+    const int kb0 = wave * nkb / DECODE_WAVES, kb1 = (wave + 1) * nkb / DECODE_WAVES;
+
+    // this lane's rows: weight row n0 + (lane & 15) (clamped to the last row:
+    // valid memory, never stored), input rows 16 mt + (lane & 15) (clamped)
+    const int nr = min(n0 + (lane & 15), p.N - 1);
+    const char* wrow = (const char*)p.W + ((int64_t)nr * p.ldw + 8 * (lane >> 4)) * 2;
+    const char* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int mr = min(16 * mt + (lane & 15), p.M - 1);
+        xrow[mt] = (const char*)p.X + ((int64_t)mr * p.ldx + 8 * (lane >> 4)) * 2;
+    }
+    const int kchunk = 8 * (lane >> 4);  // this lane's k offset within a k-block
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    constexpr int DECODE_BATCH = decode_batch(MT);
+    for (int kb = kb0; kb < kb1; kb += DECODE_BATCH) {
+        u32x4 wf[DECODE_BATCH], xf[DECODE_BATCH][MT];
+#pragma unroll
+        for (int i = 0; i < DECODE_BATCH; ++i) {
+            const int k = (kb + i) * 32 + kchunk;
+            const bool in = kb + i < kb1 && k < p.K;  // K % 8 == 0: a chunk is all in or all out
+            wf[i] = in ? load16(wrow + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                xf[i][mt] = in ? load16(xrow[mt] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < DECODE_BATCH; ++i)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[mt], wf[i], xf[i][mt]);
+    }
+
+    // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each block
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[wave][mt][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[mt][e];
+    __syncthreads();
+
+    // output (m, n0 + j) for t = 16 m + j: 16 consecutive columns per row
+    for (int t = tid; t < 16 * p.M; t += DECODE_WAVES * 64) {
+        const int m = t >> 4, j = t & 15, n = n0 + j;
+        if (n >= p.N) continue;
+        const int mt = m >> 4, ml = m & 15;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < DECODE_WAVES; ++w) s += part[w][mt][j * 16 + ml];  // m < 16 MT
+        const int64_t idx = (int64_t)m * p.ldc + n;
+        if (p.c_type == OUT_F32) {
+            float* c = (float*)p.C + idx;
+            *c = apply_epilogue<DT>(p.ep, s, p.ep.beta != 0.0f ? *c : 0.0f, n);
+        } else if (p.c_type == OUT_F16) {
+            _Float16* c = (_Float16*)p.C + idx;
+            *c = (_Float16)apply_epilogue<DT>(p.ep, s, p.ep.beta != 0.0f ? (float)*c : 0.0f, n);
+        } else {
+            __bf16* c = (__bf16*)p.C + idx;
+            *c = (__bf16)apply_epilogue<DT>(p.ep, s, p.ep.beta != 0.0f ? (float)*c : 0.0f, n);
+        }
+    }
+}
+
+}  // namespace dge

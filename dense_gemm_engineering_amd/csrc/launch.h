@@ -8,6 +8,7 @@
 #include "ladder.h"
 #include "mfma_gemm.h"
 #include "skinny.h"
+#include "decode.h"
 
 namespace dge {
 
@@ -57,6 +58,9 @@ hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int g
 // Allows every skinny instance up to 160 KB of dynamic LDS.  Called once per
 // device at library initialisation, never from inside a launch sequence.
 hipError_t skinny_init();
+// Decode-shaped kernel: 1 <= M <= 64, N x K 16-bit weight, one workgroup per
+// 16 weight rows.
+hipError_t launch_decode(int dt, const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s);
 hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s);

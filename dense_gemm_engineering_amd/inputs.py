@@ -18,6 +18,8 @@ Workloads (all row-major; w is the seed family):
                            scales fp16(|N(0, 0.02)|) and codes uniform 0..15
   tall_skinny (w=5)        X 65536 x 160 and W 160 x N (N = 160 or 32), both
                            N(0,1)/sqrt(160) fp16; bias fp16 N(0, 0.1)
+  decode_shape (w=6)       X M x 4096 fp16 N(0,1), M in {1, 8, 16, 32, 64}; one
+                           4096 x 4096 (N x K) fp16 weight N(0,1)/sqrt(4096)
 """
 import numpy as np
 
@@ -115,6 +117,18 @@ def prefill_projection(shape="up", M=2048):
     A = normal((M, K), "f16", 4, OP_A, v)
     q = q4_weights(N, K, 4, v)
     return A, q, N, K
+
+
+DECODE_ROWS = (1, 8, 16, 32, 64)
+
+
+def decode_shape(M=1, N=4096, K=4096):
+    """Decode-shaped inputs: X (M x K) fp16 N(0,1) and an N x K fp16 weight
+    N(0,1)/sqrt(K) (one 4096 x 4096 layer times M input vectors)."""
+    v = DECODE_ROWS.index(M) if M in DECODE_ROWS else 9
+    X = normal((M, K), "f16", 6, OP_A, v)
+    W = normal((N, K), "f16", 6, OP_B, 0, std=1.0 / np.sqrt(K))
+    return X, W
 
 
 def tall_skinny(N=160, M=65536, K=160):

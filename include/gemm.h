@@ -96,11 +96,20 @@ typedef enum {
     GEMM_ALGO_MFMA_DIRECT = 4, /* macro tiles fed by direct global->LDS loads (fp16/bf16,
                                   full tiles, 16-byte aligned operands); other problems
                                   run as GEMM_ALGO_MFMA.  AUTO uses it when eligible. */
-    GEMM_ALGO_SKINNY = 5      /* tall-skinny kernel: W resident in LDS, X streamed into
+    GEMM_ALGO_SKINNY = 5,     /* tall-skinny kernel: W resident in LDS, X streamed into
                                  the MFMA operands (fp16/bf16, K a multiple of 32 up to
                                  256, N <= 256, A 16-byte aligned with lda % 8 == 0);
                                  other problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO uses
                                  it for M >= 4096 and M >= 8N when eligible. */
+    GEMM_ALGO_DECODE = 6      /* decode shape: 1 <= M <= 64 input rows against an N x K
+                                 weight (trans_b = 1, fp16/bf16, K % 8 == 0, A and B
+                                 16-byte aligned with lda, ldb % 8 == 0), W streamed
+                                 from memory straight into the MFMA operands, K split
+                                 over 8 waves and summed in a fixed order; other
+                                 problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO uses it
+                                 whenever eligible ("Matrix Multiplication: The
+                                 Operation Behind Modern AI", "The shape a language
+                                 model actually runs"). */
 } gemm_algo_t;
 
 /* Tile configurations of the MFMA family (macro tile BM x BN, waves). */
