@@ -55,6 +55,9 @@ def lib():
         L.oracle_gemm.restype = i32
         L.oracle_dequant_q4.argtypes = [vp, i64, i64, vp, i64]
         L.oracle_dequant_q4.restype = i32
+        for name in ("oracle_dequant_q6_k", "oracle_dequant_q4_k"):
+            getattr(L, name).argtypes = [vp, i64, i64, vp, i64]
+            getattr(L, name).restype = i32
         _lib = L
     return _lib
 
@@ -135,6 +138,27 @@ def dequant_q4(q, rows, cols):
     rc = lib().oracle_dequant_q4(_ptr(q), rows, cols, _ptr(out), cols)
     if rc != 0:
         raise ValueError("oracle_dequant_q4 rejected the shape")
+    return out
+
+
+QTYPES = {"q4_0": (32, 18), "q4_k": (256, 144), "q6_k": (256, 210)}  # weights, bytes per block
+
+
+def dequant(qtype, q, rows, cols):
+    """Raw blocks of a weight type ("q4_0", "q4_k", "q6_k") -> (rows, cols)
+    binary16 bits."""
+    if qtype == "q4_0":
+        return dequant_q4(q, rows, cols)
+    per, nbytes = QTYPES[qtype]
+    q = np.ascontiguousarray(q, dtype=np.uint8).reshape(-1)
+    if cols % per != 0:
+        raise ValueError("cols must be a multiple of %d" % per)
+    if q.size != rows * (cols // per) * nbytes:
+        raise ValueError("expected %d bytes, got %d" % (rows * (cols // per) * nbytes, q.size))
+    out = np.empty((rows, cols), dtype=np.uint16)
+    fn = lib().oracle_dequant_q6_k if qtype == "q6_k" else lib().oracle_dequant_q4_k
+    if fn(_ptr(q), rows, cols, _ptr(out), cols) != 0:
+        raise ValueError("dequant rejected the shape")
     return out
 
 

@@ -31,6 +31,27 @@
  *    its high nibble; a code q in 0..15 stands for d*(q-8).  The product is
  *    exact in binary64 and is rounded once, to nearest-even, to binary16.
  *
+ *  - K-quant dequantisation (same page, §3.2: one dequant kernel per weight
+ *    type; float arithmetic, then one conversion to binary16).  256 weights
+ *    per super-block:
+ *      q6_K, 210 bytes: ql[128] low 4 bits, qh[64] high 2 bits, 16 int8
+ *        sub-block scales sc[16] at byte 192, binary16 d at byte 208; weight
+ *        = d * sc * (q - 32) with q = low | high << 4.  The page names the
+ *        interleaved addressing (half, quarter tt, 16-group) without printing
+ *        it; the reading taken, which matches every field it does show (low
+ *        nibble for tt < 2, high nibble otherwise, high bits qh >> 2 tt):
+ *        weight e = 128 h + 32 tt + l (l < 32) takes ql[64 h + 32 (tt & 1) +
+ *        l], qh[32 h + l] and sc[8 h + 2 tt + l / 16].  d * sc * (q - 32)
+ *        has at most 24 significant bits, so it is exact and rounds once.
+ *      q4_K, 144 bytes (the pages name the type and its dmin but print no
+ *        layout; the reading taken is the K-quant layout): binary16 d and
+ *        dmin, 12 bytes packing a 6-bit scale sc_j and 6-bit min m_j for 8
+ *        sub-blocks of 32, then qs[128]; sub-blocks 2p and 2p + 1 take the
+ *        low and high nibbles of qs[32 p .. 32 p + 31]; weight =
+ *        RNE16(RNE32(d sc_j q - dmin m_j)): d sc_j q and dmin m_j are exact
+ *        in binary32, the difference is rounded to binary32 as the page's
+ *        float arithmetic does, then once more to binary16.
+ *
  *  - Rounding.  binary64 -> binary16 / bfloat16 / binary32, round to nearest,
  *    ties to even, with gradual underflow and overflow to infinity.
  *
@@ -294,6 +315,82 @@ int oracle_dequant_q4(const uint8_t* q, int64_t rows, int64_t cols, uint16_t* ou
                 const int lo = blk[2 + i] & 15, hi = blk[2 + i] >> 4;
                 out[r * ldo + 32 * b + i] = oracle_f64_to_f16(d * (double)(lo - 8));
                 out[r * ldo + 32 * b + 16 + i] = oracle_f64_to_f16(d * (double)(hi - 8));
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------- K-quant dequant */
+
+/* q6_K: rows x cols weights (cols % 256 == 0), super-blocks of 210 bytes,
+ * row-major by (row, super-block).  Returns -1 for a bad shape. */
+int oracle_dequant_q6_k(const uint8_t* q, int64_t rows, int64_t cols, uint16_t* out,
+                        int64_t ldo) {
+    if (cols % 256 != 0) return -1;
+    const int64_t nsb = cols / 256;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nsb; ++b) {
+            const uint8_t* blk = q + 210 * (r * nsb + b);
+            const uint8_t* ql = blk;
+            const uint8_t* qh = blk + 128;
+            const int8_t* sc = (const int8_t*)(blk + 192);
+            const double d = oracle_f16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+            for (int e = 0; e < 256; ++e) {
+                const int h = e / 128, tt = (e % 128) / 32, l = e % 32;
+                const int byte = ql[64 * h + 32 * (tt & 1) + l];
+                const int low = tt < 2 ? (byte & 15) : (byte >> 4);
+                const int high = (qh[32 * h + l] >> (2 * tt)) & 3;
+                const int code = (low | (high << 4)) - 32;
+                const double v = d * (double)sc[8 * h + 2 * tt + l / 16] * (double)code;
+                out[r * ldo + 256 * b + e] = oracle_f64_to_f16(v);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The 6-bit scale and min of sub-block j (0..7) from the 12 packed bytes:
+ * sub-blocks 0..3 keep their scale and min in the low 6 bits of bytes j and
+ * j + 4; sub-blocks 4..7 keep the low 4 bits of each in byte j + 4 (scale in
+ * the low nibble, min in the high one) and the top 2 bits in the top 2 bits
+ * of bytes j - 4 (scale) and j (min). */
+static void q4_k_scale_min(const uint8_t* s12, int j, int* sc, int* m) {
+    if (j < 4) {
+        *sc = s12[j] & 63;
+        *m = s12[j + 4] & 63;
+    } else {
+        *sc = (s12[j + 4] & 15) | ((s12[j - 4] >> 6) << 4);
+        *m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+    }
+}
+
+/* q4_K: rows x cols weights (cols % 256 == 0), super-blocks of 144 bytes. */
+int oracle_dequant_q4_k(const uint8_t* q, int64_t rows, int64_t cols, uint16_t* out,
+                        int64_t ldo) {
+    if (cols % 256 != 0) return -1;
+    const int64_t nsb = cols / 256;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nsb; ++b) {
+            const uint8_t* blk = q + 144 * (r * nsb + b);
+            const double d = oracle_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+            const double dmin = oracle_f16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+            const uint8_t* qs = blk + 16;
+            for (int e = 0; e < 256; ++e) {
+                const int p = e / 64, w = e % 64;
+                const int j = 2 * p + (w >= 32);
+                const int byte = qs[32 * p + w % 32];
+                const int code = w < 32 ? (byte & 15) : (byte >> 4);
+                int sc, m;
+                q4_k_scale_min(blk + 4, j, &sc, &m);
+                const double t = d * (double)sc * (double)code; /* <= 21 bits: exact */
+                const double u = dmin * (double)m;              /* <= 17 bits: exact */
+                /* t - u in binary64 is exact when the operands are within 2^29 of
+                 * each other; otherwise the smaller is below half a binary32 ulp of
+                 * the larger (an exact binary32 value) and both this difference and
+                 * the exact one round to the larger in binary32. */
+                const double f32 = oracle_f32_to_f64(oracle_f64_to_f32(t - u));
+                out[r * ldo + 256 * b + e] = oracle_f64_to_f16(f32);
             }
         }
     }
