@@ -54,6 +54,16 @@ def dequant_alg_bytes(rows, cols):
     return rows * cols / 32 * 18 + rows * cols * 2.0
 
 
+KQ_BLOCK = {"q4_k": (256, 144), "q6_k": (256, 210)}
+
+
+def kquant_alg_bytes(qtype, rows, cols):
+    """Super-block format -> fp16: the block bytes read once, 2 bytes per
+    weight written."""
+    w, nb = KQ_BLOCK[qtype]
+    return rows * cols / w * nb + rows * cols * 2.0
+
+
 def prefill_stack_tokens_per_s(t_attn, t_up, t_down, tokens=2048, layers=32):
     """tokens / (layers x [4 square projections + 2 up-projections + 1 down]).
 
@@ -183,6 +193,39 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
         "tok_s_dequant_per_call": prefill_stack_tokens_per_s(t["attn"], t["up"], t["down"]),
         "tok_s_gemm_only": prefill_stack_tokens_per_s(g["attn"], g["up"], g["down"]),
         "tok_s_fused": prefill_stack_tokens_per_s(f["attn"], f["up"], f["down"])}
+    return out
+
+
+def bench_kquant(dge, inputs, torch, steps, prefill, rotate_bytes=300e6):
+    """The super-block formats: dequant_f16 per prefill shape (HBM-cold by
+    rotating weight sets); two-pass tok/s with the fp16 GEMM time measured by
+    the prefill leg (the GEMM is the same one)."""
+    out = {}
+    for qtype in ("q4_k", "q6_k"):
+        res = {}
+        for shape in ("up", "attn", "down"):
+            _, q, N, K = inputs.kquant_projection(qtype, shape, M=1)
+            alg = kquant_alg_bytes(qtype, N, K)
+            nset = max(1, int(np.ceil(rotate_bytes / alg)))
+            qs = [torch.from_numpy(q).cuda() for _ in range(nset)]
+            ws = [torch.empty((N, K), dtype=torch.float16, device="cuda") for _ in range(nset)]
+            it = [0]
+
+            def deq():
+                i = it[0] % nset
+                it[0] += 1
+                dge.dequant_f16(qtype, qs[i], N, K, out=ws[i])
+
+            td, _ = time_launches(deq, steps, 3, torch)
+            tg = prefill[shape]["gemm_us"] * 1e-6
+            res[shape] = {"dequant_us": td * 1e6, "dequant_GBs": alg / td / 1e9,
+                          "dequant_hbm_frac": alg / td / 1e9 / HBM_PEAK_GBS,
+                          "tok_s_dequant_per_call": 2048 / (td + tg)}
+            del qs, ws
+        t = {k: res[k]["dequant_us"] * 1e-6 + prefill[k]["gemm_us"] * 1e-6 for k in res}
+        res["stack_7b_like"] = {
+            "tok_s_dequant_per_call": prefill_stack_tokens_per_s(t["attn"], t["up"], t["down"])}
+        out[qtype] = res
     return out
 
 
@@ -344,6 +387,8 @@ def main():
     if not args.no_extra:
         extra_steps = max(10, min(args.steps, 30))
         line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps)
+        line["prefill_kquant"] = bench_kquant(dge, inputs, torch, extra_steps,
+                                              line["prefill_2048"])
         line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps)
         line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps)
         line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)

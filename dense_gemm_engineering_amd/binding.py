@@ -21,10 +21,11 @@ IN = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
 ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "mfma": 3, "mfma_direct": 4, "skinny": 5,
         "decode": 6}
 TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x256w8": 5}
+QTYPE = {"q4_0": 0, "q4_k": 1, "q6_k": 2, "q6_k_224": 3}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "dequant_q4_f16", "prefill_q4_f16",
-           "gemm_q4_f16",
+           "gemm_q4_f16", "dequant_f16", "prefill_f16",
            "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_status_string", "gemm_init")
 
 
@@ -67,6 +68,10 @@ def lib():
         L.gemm_q4_f16.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, i32, i32, vp, vp, sz,
                                   ctypes.POINTER(Tuning), vp]
         L.gemm_q4_f16.restype = i32
+        L.dequant_f16.argtypes = [i32, vp, vp, i64, i64, i64, vp]
+        L.dequant_f16.restype = i32
+        L.prefill_f16.argtypes = [i32] + L.prefill_q4_f16.argtypes
+        L.prefill_f16.restype = i32
         L.gemm_workspace_size.argtypes = [i64, i64, i64, i32]
         L.gemm_workspace_size.restype = sz
         L.gemm_workspace_size_splits.argtypes = [i64, i64, i32]
@@ -194,6 +199,32 @@ def prefill_q4_f16(A, q, N, K, w16=None, C=None, *, out_dtype=torch.float16, epi
     _check(lib().prefill_q4_f16(M, N, K, _ptr(A), _ld(A, "A"), _ptr(q), _ptr(w16), _ptr(C),
                                 _ld(C, "C"), OUT[C.dtype], EPI[epi], _ptr(bias), _ptr(workspace),
                                 ws_bytes, _stream(stream)), "prefill_q4_f16")
+    return C
+
+
+def dequant_f16(qtype, q, rows, cols, out=None, stream=None):
+    """q: uint8 device tensor of blocks in format qtype ("q4_0", "q4_k",
+    "q6_k", "q6_k_224") -> (rows, cols) fp16."""
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=q.device)
+    ldo = _ld(out, "out") if out.numel() else cols
+    _check(lib().dequant_f16(QTYPE[qtype], _ptr(q), _ptr(out), rows, cols, ldo, _stream(stream)),
+           "dequant_f16")
+    return out
+
+
+def prefill_f16(qtype, A, q, N, K, w16=None, C=None, *, out_dtype=torch.float16, epi="none",
+                bias=None, workspace=None, stream=None):
+    """C = epi(A @ dequant_f16(qtype, q)^T); w16 is the caller's fp16 N x K scratch."""
+    M = A.shape[0]
+    if w16 is None:
+        w16 = torch.empty((N, K), dtype=torch.float16, device=A.device)
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().prefill_f16(QTYPE[qtype], M, N, K, _ptr(A), _ld(A, "A"), _ptr(q), _ptr(w16),
+                             _ptr(C), _ld(C, "C"), OUT[C.dtype], EPI[epi], _ptr(bias),
+                             _ptr(workspace), ws_bytes, _stream(stream)), "prefill_f16")
     return C
 
 

@@ -530,11 +530,45 @@ gemm_status_t dequant_q4_f16(const void* q, void* out, int64_t rows, int64_t col
         launch_dequant_q4(q, out, rows, cols, ldo, vec_out, (hipStream_t)stream));
 }
 
-gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                             const void* q, void* w16, void* C, int64_t ldc, gemm_out_t c_type,
-                             gemm_epilogue_t epi, const void* bias, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return GEMM_ERR_INVALID_VALUE;
+// Block width (weights) and size (bytes) of a gemm_qtype_t; false if unknown.
+static bool qformat(int qtype, int64_t* width, int64_t* bytes) {
+    switch (qtype) {
+        case GEMM_Q4_0: *width = 32; *bytes = 18; return true;
+        case GEMM_Q4_K: *width = 256; *bytes = 144; return true;
+        case GEMM_Q6_K: *width = 256; *bytes = 210; return true;
+        case GEMM_Q6_K_224: *width = 256; *bytes = 224; return true;
+        default: return false;
+    }
+}
+
+gemm_status_t dequant_f16(gemm_qtype_t qtype, const void* q, void* out, int64_t rows,
+                          int64_t cols, int64_t ldo, void* stream) {
+    int64_t w = 0, nb = 0;
+    if (!qformat((int)qtype, &w, &nb)) return GEMM_ERR_INVALID_VALUE;
+    if (qtype == GEMM_Q4_0) return dequant_q4_f16(q, out, rows, cols, ldo, stream);
+    if (rows < 0 || cols < 0 || cols % w != 0 || ldo < cols) return GEMM_ERR_INVALID_VALUE;
+    if (rows > kMaxDim || cols > kMaxDim || ldo > kMaxDim * 64) return GEMM_ERR_INVALID_VALUE;
+    if (rows == 0 || cols == 0) return GEMM_OK;
+    if (!q || !out || ((uintptr_t)out & 1)) return GEMM_ERR_INVALID_VALUE;
+    const Range rq = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(rows * (cols / w) * nb)};
+    if (overlaps(rq, span(out, rows, cols, ldo, 2))) return GEMM_ERR_INVALID_VALUE;
+    gemm_status_t st = forced_failure();
+    if (st != GEMM_OK) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    const int vec_out = aligned16(out) && ldo % 8 == 0;
+    const int kq = qtype == GEMM_Q6_K ? KQ_Q6_K : qtype == GEMM_Q6_K_224 ? KQ_Q6_K_224 : KQ_Q4_K;
+    return launch_status(
+        launch_dequant_kq(kq, q, out, rows, cols, ldo, vec_out, (hipStream_t)stream));
+}
+
+gemm_status_t prefill_f16(gemm_qtype_t qtype, int64_t M, int64_t N, int64_t K, const void* A,
+                          int64_t lda, const void* q, void* w16, void* C, int64_t ldc,
+                          gemm_out_t c_type, gemm_epilogue_t epi, const void* bias,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    int64_t w = 0, nb = 0;
+    if (!qformat((int)qtype, &w, &nb)) return GEMM_ERR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0 || K % w != 0) return GEMM_ERR_INVALID_VALUE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_VALUE;
     if (M == 0 || N == 0) return GEMM_OK;
     if (K > 0 && (!q || !w16)) return GEMM_ERR_INVALID_VALUE;
@@ -545,14 +579,22 @@ gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int
     if (st != GEMM_OK) return st;
     if (K > 0) {
         const Range rw = span(w16, N, K, K, 2);
-        const Range rq = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(N * (K / 32) * 18)};
+        const Range rq = {(uintptr_t)q, (uintptr_t)q + (uintptr_t)(N * (K / w) * nb)};
         if (overlaps(rw, rq) || overlaps(rw, span(A, M, K, lda, 2)) ||
             overlaps(rw, span(C, M, N, ldc, out_bytes((int)c_type))))
             return GEMM_ERR_INVALID_VALUE;
-        st = dequant_q4_f16(q, w16, N, K, K, stream);
+        st = dequant_f16(qtype, q, w16, N, K, K, stream);
         if (st != GEMM_OK) return st;
     }
     return run_gemm(g, nullptr);
+}
+
+gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* q, void* w16, void* C, int64_t ldc, gemm_out_t c_type,
+                             gemm_epilogue_t epi, const void* bias, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return prefill_f16(GEMM_Q4_0, M, N, K, A, lda, q, w16, C, ldc, c_type, epi, bias, workspace,
+                       workspace_bytes, stream);
 }
 
 gemm_status_t gemm_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

@@ -86,4 +86,146 @@ __global__ __launch_bounds__(256) void dequant_q4_f16_kernel(const uint8_t* __re
     }
 }
 
+
+// K-quant super-blocks (256 weights) -> binary16, same page, §3.2 (one
+// dequant kernel per weight type, float arithmetic then one conversion to
+// binary16).
+//   q6_K (QT = KQ_Q6_K, or KQ_Q6_K_224 for the same bytes padded to a
+//     224-byte stride), 210 bytes: ql[128] low 4 bits, qh[64] high 2 bits,
+//     int8 scales sc[16] at byte 192, binary16 d at 208.  Weight e = 128 h +
+//     32 tt + l takes the low (tt < 2) or high nibble of ql[64 h + 32 (tt & 1)
+//     + l], the 2 bits (qh[32 h + l] >> 2 tt) & 3 and sc[8 h + 2 tt + l / 16];
+//     value d * sc * (q - 32), exact in fp32 (<= 24 significant bits), rounded
+//     once to binary16.
+//   q4_K (QT = KQ_Q4_K), 144 bytes: binary16 d and dmin, 12 bytes of 6-bit
+//     scales and mins for 8 sub-blocks of 32, qs[128]; sub-blocks 2p and 2p + 1
+//     take the low and high nibbles of qs[32 p .. 32 p + 31]; value d sc q -
+//     dmin m in fp32 (both products exact, the difference rounded once), then
+//     rounded to binary16: two roundings, which differ from one rounding of
+//     the exact value when the binary32 result is a binary16 tie.
+// A workgroup stages SB consecutive super-blocks (SB a multiple of 8: 1680,
+// 1792 or 1152 bytes per 8, multiples of 16) into LDS with coalesced loads; task c
+// then decodes the 16-byte output chunk c % 32 (weights 8 (c % 32) .. + 7) of
+// super-block c / 32, consecutive threads writing consecutive chunks.
+constexpr int KQ_STEP = 16;    // super-blocks per workgroup step
+constexpr int KQ_GRID = 2048;  // most workgroups a launch uses
+
+template <int QT> struct KQuant;
+// BYTES: block stride; Q6: the q6_K fields (the 224-byte layout is the 210
+// bytes of a q6_K super-block followed by 14 unused bytes)
+template <> struct KQuant<KQ_Q4_K> { static constexpr int BYTES = 144; static constexpr bool Q6 = false; };
+template <> struct KQuant<KQ_Q6_K> { static constexpr int BYTES = 210; static constexpr bool Q6 = true; };
+template <> struct KQuant<KQ_Q6_K_224> { static constexpr int BYTES = 224; static constexpr bool Q6 = true; };
+
+template <int QT, int SB>
+__global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __restrict__ q,
+                                                             uint16_t* __restrict__ out,
+                                                             int64_t rows, int64_t cols,
+                                                             int64_t ldo, int flags) {
+    constexpr int BYTES = KQuant<QT>::BYTES;
+    static_assert(SB % 8 == 0, "groups of 8 super-blocks keep 16-byte alignment");
+    __shared__ __attribute__((aligned(16))) uint8_t raw[SB * BYTES];
+    const bool vec_in = (flags & 1) != 0, vec_out = (flags & 2) != 0;
+    const int tid = threadIdx.x;
+    const int64_t nsb = cols / 256;
+    const int64_t total = rows * nsb;
+    // 16-byte input chunks per thread per step; with aligned input the next
+    // step's chunks are loaded into registers while this step is decoded
+    constexpr int NCH = (SB * BYTES + 16 * 256 - 1) / (16 * 256);
+    u32x4 pre[NCH];
+    auto fetch = [&](int64_t g) {
+        const int nb = (int)(total - g < SB ? total - g : SB);
+        const uint8_t* src = q + BYTES * g;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + 256 * i;
+            if (c < nb * BYTES / 16) pre[i] = *(const u32x4*)(src + 16 * c);
+        }
+    };
+    const int64_t gstep = (int64_t)gridDim.x * SB;
+    if (vec_in && (int64_t)blockIdx.x * SB < total) fetch((int64_t)blockIdx.x * SB);
+    for (int64_t g0 = (int64_t)blockIdx.x * SB; g0 < total; g0 += gstep) {
+        const int nblk = (int)(total - g0 < SB ? total - g0 : SB);
+        const int bytes = nblk * BYTES;
+        const uint8_t* src = q + BYTES * g0;
+        int done = 0;
+        if (vec_in) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = tid + 256 * i;
+                if (c < bytes / 16) *(u32x4*)(raw + 16 * c) = pre[i];
+            }
+            done = bytes / 16 * 16;
+        }
+        for (int i = done + tid; i < bytes; i += 256) raw[i] = src[i];
+        // first super-block of the step: row r0, column c0 (one 64-bit division per step)
+        const int64_t r0 = g0 / nsb;
+        const uint32_t c0 = (uint32_t)(g0 - r0 * nsb), unsb = (uint32_t)nsb;
+        __syncthreads();
+        if (vec_in && g0 + gstep < total) fetch(g0 + gstep);
+        for (int task = tid; task < 32 * nblk; task += 256) {
+            const int sbl = task >> 5, c = task & 31;
+            const uint8_t* blk = raw + BYTES * sbl;
+            const int e0 = 8 * c;
+            uint16_t h[8];
+            if constexpr (KQuant<QT>::Q6) {
+                const int hh = e0 / 128, tt = (e0 % 128) / 32, l0 = e0 % 32;
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[208] | (blk[209] << 8)));
+                const float dsc = d * (float)(int8_t)blk[192 + 8 * hh + 2 * tt + l0 / 16];  // exact
+                const uint8_t* ql = blk + 64 * hh + 32 * (tt & 1) + l0;
+                const uint8_t* qh = blk + 128 + 32 * hh + l0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int low = tt < 2 ? (ql[i] & 15) : (ql[i] >> 4);
+                    const int code = (low | (((qh[i] >> (2 * tt)) & 3) << 4)) - 32;
+                    // exact product, one rounding; the empty asm keeps the
+                    // multiply a multiply (folded into a mixed-precision FMA it
+                    // adds +0, which turns a -0 product into +0)
+                    float v = dsc * (float)code;
+                    __asm__("" : "+v"(v));
+                    h[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                }
+            } else {
+                const int p = e0 / 64, w0 = e0 % 64, j = 2 * p + (w0 >= 32);
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[0] | (blk[1] << 8)));
+                const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[2] | (blk[3] << 8)));
+                const uint8_t* s12 = blk + 4;
+                int sc, m;
+                if (j < 4) {
+                    sc = s12[j] & 63;
+                    m = s12[j + 4] & 63;
+                } else {
+                    sc = (s12[j + 4] & 15) | ((s12[j - 4] >> 6) << 4);
+                    m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+                }
+                const float a = d * (float)sc, u = dmin * (float)m;  // both exact
+                const uint8_t* qs = blk + 16 + 32 * p + (w0 & 31);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int code = w0 < 32 ? (qs[i] & 15) : (qs[i] >> 4);
+                    // a * code is exact, so the fused form rounds the difference
+                    // once, to binary32; the empty asm keeps that binary32 value
+                    // (otherwise the compiler folds fma and conversion into one
+                    // mixed-precision FMA that rounds straight to binary16, which
+                    // differs at binary16 ties)
+                    float v = __builtin_fmaf(a, (float)code, -u);
+                    __asm__("" : "+v"(v));
+                    h[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                }
+            }
+            const uint32_t cc = c0 + (uint32_t)sbl;  // < nsb + SB
+            const uint32_t dr = cc / unsb;
+            uint16_t* dst = out + (r0 + dr) * ldo + 256 * (cc - dr * unsb) + e0;
+            if (vec_out) {
+                *(u32x4*)dst = (u32x4){(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                                       (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16)};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dst[i] = h[i];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace dge

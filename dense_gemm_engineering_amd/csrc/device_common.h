@@ -11,6 +11,8 @@ namespace dge {
 enum : int { IN_F16 = 0, IN_BF16 = 1, IN_F32 = 2 };
 enum : int { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 enum : int { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU = 2 };
+// block-quantised weight formats (numbered as gemm_qtype_t)
+enum : int { KQ_Q4_0 = 0, KQ_Q4_K = 1, KQ_Q6_K = 2, KQ_Q6_K_224 = 3 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -66,4 +66,25 @@ hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t col
     return hipGetLastError();
 }
 
+hipError_t launch_dequant_kq(int qtype, const void* q, void* out, int64_t rows, int64_t cols,
+                             int64_t ldo, int vec_out, hipStream_t s) {
+    constexpr int SB = KQ_STEP;
+    const int64_t total = rows * (cols / 256);
+    int64_t blocks = (total + SB - 1) / SB;
+    // 8 resident workgroups per CU of a 256-CU part: each takes several
+    // steps, so its register prefetch of the next step overlaps the decode
+    if (blocks > KQ_GRID) blocks = KQ_GRID;
+    const int flags = (((uintptr_t)q & 15) == 0 ? 1 : 0) | (vec_out ? 2 : 0);
+    if (qtype == KQ_Q6_K)
+        hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q6_K, SB>), dim3((unsigned)blocks), dim3(256), 0,
+                           s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
+    else if (qtype == KQ_Q6_K_224)
+        hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q6_K_224, SB>), dim3((unsigned)blocks), dim3(256),
+                           0, s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
+    else
+        hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q4_K, SB>), dim3((unsigned)blocks), dim3(256), 0,
+                           s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
+    return hipGetLastError();
+}
+
 }  // namespace dge

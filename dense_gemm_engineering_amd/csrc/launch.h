@@ -68,5 +68,8 @@ hipError_t launch_splitk_fixup(int dt, const SimpleArgs& a, const float* ws, int
                                hipStream_t s);
 hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
                              int vec_out, hipStream_t s);
+// K-quant super-blocks (qtype KQ_Q4_K, KQ_Q6_K or KQ_Q6_K_224), cols % 256 == 0.
+hipError_t launch_dequant_kq(int qtype, const void* q, void* out, int64_t rows, int64_t cols,
+                             int64_t ldo, int vec_out, hipStream_t s);
 
 }  // namespace dge

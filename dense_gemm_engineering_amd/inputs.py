@@ -20,6 +20,13 @@ Workloads (all row-major; w is the seed family):
                            N(0,1)/sqrt(160) fp16; bias fp16 N(0, 0.1)
   decode_shape (w=6)       X M x 4096 fp16 N(0,1), M in {1, 8, 16, 32, 64}; one
                            4096 x 4096 (N x K) fp16 weight N(0,1)/sqrt(4096)
+  kquant_projection (w=7)  prefill_projection's A and shapes with the weight in
+                           a 256-weight super-block format (q4_k, q6_k or
+                           q6_k at a 224-byte stride):
+                           every byte uniform, then each binary16 scale
+                           field overwritten with fp16(|N(0, s)|) (q6_k d:
+                           s = 2e-5; q4_k d and dmin: s = 4e-5), so weights
+                           are of the q4 workload's magnitude
 """
 import numpy as np
 
@@ -87,6 +94,36 @@ def q4_weights(rows, cols, workload=4, variant=0, scale_std=0.02):
     scale_bits = to_bits(d, "f16")
     codes = rng(workload, OP_CODE, variant).integers(0, 16, size=(rows, nb, 32))
     return pack_q4(scale_bits, codes)
+
+
+# Super-block formats: (weights, bytes, byte offsets of the binary16 scale
+# fields, scale std)
+KQUANT = {"q4_k": (256, 144, (0, 2), 4e-5), "q6_k": (256, 210, (208,), 2e-5),
+          "q6_k_224": (256, 224, (208,), 2e-5)}
+
+
+def kquant_weights(qtype, rows, cols, workload=7, variant=0):
+    """Synthetic rows x cols weight in a super-block format: uniform random
+    bytes (codes, sub-block scales and mins) with sane binary16 scales."""
+    w, nbytes, offs, std = KQUANT[qtype]
+    assert cols % w == 0
+    nsb = rows * (cols // w)
+    q = rng(workload, OP_CODE, variant).integers(0, 256, size=(nsb, nbytes), dtype=np.uint8)
+    r = rng(workload, OP_SCALE, variant)
+    for off in offs:
+        bits = to_bits(np.abs(r.standard_normal(nsb) * std), "f16")
+        q[:, off] = bits & 0xFF
+        q[:, off + 1] = bits >> 8
+    return q.reshape(-1)
+
+
+def kquant_projection(qtype, shape="up", M=2048):
+    """prefill_projection with the weight as super-blocks: A, q, N, K."""
+    N, K = PREFILL_SHAPES[shape]
+    v = {"up": 0, "attn": 1, "down": 2}[shape]
+    A = normal((M, K), "f16", 4, OP_A, v)
+    q = kquant_weights(qtype, N, K, 7, v + {"q4_k": 0, "q6_k": 3, "q6_k_224": 6}[qtype])
+    return A, q, N, K
 
 
 # ----------------------------------------------------------------- workloads

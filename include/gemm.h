@@ -22,6 +22,11 @@
  *     B-tile producer, so the binary16 weight is never written to memory:
  *     the dequant-in-GEMM successor that §2.3 of the same page names for
  *     the three-pass cost of the dequant-then-GEMM route.
+ *   dequant_f16 / prefill_f16:
+ *     the same two entry points for any of the page's block formats: q4_0
+ *     and the 256-weight super-block formats q4_K and q6_K, one dequant
+ *     kernel per format in front of the same GEMM (same page, §2.3 and §3.1
+ *     name the formats and the per-format kernel; §3.2 prints the q6_K one).
  *
  * Conventions (all entry points)
  *   - Row-major throughout; leading dimensions are in elements.
@@ -85,6 +90,15 @@ typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_BIAS = 1, GEMM_EPI_BIAS_GELU = 2 } ge
 typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_F16 = 1, GEMM_OUT_BF16 = 2 } gemm_out_t;
 
 typedef enum { GEMM_IN_F16 = 0, GEMM_IN_BF16 = 1, GEMM_IN_F32 = 2 } gemm_in_t;
+
+/* Block-quantised weight formats of dequant_f16 / prefill_f16 (layouts at
+ * dequant_f16). */
+typedef enum {
+    GEMM_Q4_0 = 0, /* 32 weights in 18 bytes */
+    GEMM_Q4_K = 1, /* 256 weights in 144 bytes */
+    GEMM_Q6_K = 2, /* 256 weights in 210 bytes */
+    GEMM_Q6_K_224 = 3 /* GEMM_Q6_K blocks padded to a 224-byte stride */
+} gemm_qtype_t;
 
 /* Kernel families, for gemm_ex's explicit selection. */
 typedef enum {
@@ -199,6 +213,50 @@ gemm_status_t gemm_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_
                           const void* q, void* C, int64_t ldc, gemm_out_t c_type,
                           gemm_epilogue_t epi, const void* bias, void* workspace,
                           size_t workspace_bytes, const gemm_tuning_t* tuning, void* stream);
+
+/* Block-quantised weight -> binary16, for every gemm_qtype_t.  q holds the
+ * rows x cols weight as consecutive blocks, row-major (block b of row r is
+ * block number r * (cols / W) + b, W weights per block), with no padding;
+ * out[r * ldo + c] receives weight (r, c).  Multi-byte fields are
+ * little-endian; "binary16" fields are IEEE half precision.
+ *   GEMM_Q4_0 (W = 32, 18 bytes): as dequant_q4_f16.
+ *   GEMM_Q6_K (W = 256, 210 bytes): ql[128] at 0, qh[64] at 128, 16 int8
+ *     scales sc at 192, binary16 d at 208.  Weight e = 128 h + 32 t + l
+ *     (h < 2, t < 4, l < 32) has the 6-bit code q whose low 4 bits are the
+ *     low (t < 2) or high (t >= 2) nibble of ql[64 h + 32 (t & 1) + l] and
+ *     whose high 2 bits are bits 2t, 2t + 1 of qh[32 h + l]; its value is
+ *     RNE16(d * sc[8 h + 2 t + l / 16] * (q - 32)), computed exactly (a
+ *     zero product keeps the IEEE sign: -0 when d * sc < 0).
+ *   GEMM_Q6_K_224 (W = 256, 224 bytes): a GEMM_Q6_K block followed by 14
+ *     bytes that are not read (the padded layout the page's q6_K kernel
+ *     takes through its block stride, §3.2).
+ *   GEMM_Q4_K (W = 256, 144 bytes): binary16 d at 0, binary16 dmin at 2,
+ *     12 bytes of packed 6-bit scales at 4, 128 code bytes qs at 16.  The
+ *     256 weights form 8 sub-blocks of 32 with a 6-bit scale s_j and min
+ *     m_j: for j < 4, s_j = byte[j] & 63 and m_j = byte[j + 4] & 63; for
+ *     j >= 4, s_j = (byte[j + 4] & 15) | (byte[j - 4] >> 6) << 4 and m_j =
+ *     (byte[j + 4] >> 4) | (byte[j] >> 6) << 4 (byte[] = the 12 bytes).
+ *     Weight e = 64 p + w (p < 4, w < 64) is in sub-block j = 2p + (w >= 32)
+ *     and has the code q = low (w < 32) or high nibble of qs[32 p + w % 32];
+ *     its value is RNE16(RNE32(d s_j q - dmin m_j)) (both products exact in
+ *     binary32, the difference rounded once to binary32, then to binary16).
+ * Requires cols % W == 0, ldo >= cols, out 2-byte aligned, q 2-byte aligned
+ * for GEMM_Q4_0 (any alignment for the K formats), q and out disjoint, and a
+ * known qtype; GEMM_ERR_INVALID_VALUE otherwise.  The results are
+ * bit-exact.  rows == 0 or cols == 0 is a successful no-op. */
+gemm_status_t dequant_f16(gemm_qtype_t qtype, const void* q, void* out, int64_t rows,
+                          int64_t cols, int64_t ldo, void* stream);
+
+/* Prefill projection for every gemm_qtype_t: w16 (caller scratch, N x K
+ * binary16, >= 2*N*K bytes) = dequant_f16(qtype, q); then C = epi(A *
+ * w16^T), A M x K fp16 (lda), C M x N (ldc, c_type), alpha = 1, beta = 0,
+ * bias as for gemm_f16.  K must be a multiple of the format's block width
+ * (32 for GEMM_Q4_0, 256 for the K formats).  Both steps are enqueued on
+ * `stream`; w16 holds the dequantised weight afterwards. */
+gemm_status_t prefill_f16(gemm_qtype_t qtype, int64_t M, int64_t N, int64_t K, const void* A,
+                          int64_t lda, const void* q, void* w16, void* C, int64_t ldc,
+                          gemm_out_t c_type, gemm_epilogue_t epi, const void* bias,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes the automatic schedule of this shape would use (0 if it
  * would not split K).  dtype is a gemm_in_t. */

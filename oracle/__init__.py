@@ -55,9 +55,10 @@ def lib():
         L.oracle_gemm.restype = i32
         L.oracle_dequant_q4.argtypes = [vp, i64, i64, vp, i64]
         L.oracle_dequant_q4.restype = i32
-        for name in ("oracle_dequant_q6_k", "oracle_dequant_q4_k"):
-            getattr(L, name).argtypes = [vp, i64, i64, vp, i64]
-            getattr(L, name).restype = i32
+        L.oracle_dequant_q6_k.argtypes = [vp, i64, i64, i64, vp, i64]
+        L.oracle_dequant_q6_k.restype = i32
+        L.oracle_dequant_q4_k.argtypes = [vp, i64, i64, vp, i64]
+        L.oracle_dequant_q4_k.restype = i32
         _lib = L
     return _lib
 
@@ -141,12 +142,13 @@ def dequant_q4(q, rows, cols):
     return out
 
 
-QTYPES = {"q4_0": (32, 18), "q4_k": (256, 144), "q6_k": (256, 210)}  # weights, bytes per block
+# weights and bytes per block; "q6_k_224" is q6_K at a 224-byte block stride
+QTYPES = {"q4_0": (32, 18), "q4_k": (256, 144), "q6_k": (256, 210), "q6_k_224": (256, 224)}
 
 
 def dequant(qtype, q, rows, cols):
-    """Raw blocks of a weight type ("q4_0", "q4_k", "q6_k") -> (rows, cols)
-    binary16 bits."""
+    """Raw blocks of a weight type ("q4_0", "q4_k", "q6_k", "q6_k_224") ->
+    (rows, cols) binary16 bits."""
     if qtype == "q4_0":
         return dequant_q4(q, rows, cols)
     per, nbytes = QTYPES[qtype]
@@ -156,8 +158,11 @@ def dequant(qtype, q, rows, cols):
     if q.size != rows * (cols // per) * nbytes:
         raise ValueError("expected %d bytes, got %d" % (rows * (cols // per) * nbytes, q.size))
     out = np.empty((rows, cols), dtype=np.uint16)
-    fn = lib().oracle_dequant_q6_k if qtype == "q6_k" else lib().oracle_dequant_q4_k
-    if fn(_ptr(q), rows, cols, _ptr(out), cols) != 0:
+    if qtype.startswith("q6_k"):
+        st = lib().oracle_dequant_q6_k(_ptr(q), rows, cols, nbytes, _ptr(out), cols)
+    else:
+        st = lib().oracle_dequant_q4_k(_ptr(q), rows, cols, _ptr(out), cols)
+    if st != 0:
         raise ValueError("dequant rejected the shape")
     return out
 

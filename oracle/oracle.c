@@ -34,7 +34,9 @@
  *  - K-quant dequantisation (same page, §3.2: one dequant kernel per weight
  *    type; float arithmetic, then one conversion to binary16).  256 weights
  *    per super-block:
- *      q6_K, 210 bytes: ql[128] low 4 bits, qh[64] high 2 bits, 16 int8
+ *      q6_K, 210 bytes (or the same 210 bytes padded to a 224-byte stride,
+ *        the two layouts the page's q6_K kernel takes through its block
+ *        stride): ql[128] low 4 bits, qh[64] high 2 bits, 16 int8
  *        sub-block scales sc[16] at byte 192, binary16 d at byte 208; weight
  *        = d * sc * (q - 32) with q = low | high << 4.  The page names the
  *        interleaved addressing (half, quarter tt, 16-group) without printing
@@ -323,15 +325,17 @@ int oracle_dequant_q4(const uint8_t* q, int64_t rows, int64_t cols, uint16_t* ou
 
 /* ---------------------------------------------------------- K-quant dequant */
 
-/* q6_K: rows x cols weights (cols % 256 == 0), super-blocks of 210 bytes,
- * row-major by (row, super-block).  Returns -1 for a bad shape. */
-int oracle_dequant_q6_k(const uint8_t* q, int64_t rows, int64_t cols, uint16_t* out,
-                        int64_t ldo) {
-    if (cols % 256 != 0) return -1;
+/* q6_K: rows x cols weights (cols % 256 == 0), super-blocks of 210 bytes
+ * placed every `stride` bytes (210, or 224 for the padded layout the same
+ * page's q6_K kernel also accepts; the bytes past 210 are ignored),
+ * row-major by (row, super-block).  Returns -1 for a bad shape or stride. */
+int oracle_dequant_q6_k(const uint8_t* q, int64_t rows, int64_t cols, int64_t stride,
+                        uint16_t* out, int64_t ldo) {
+    if (cols % 256 != 0 || stride < 210) return -1;
     const int64_t nsb = cols / 256;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nsb; ++b) {
-            const uint8_t* blk = q + 210 * (r * nsb + b);
+            const uint8_t* blk = q + stride * (r * nsb + b);
             const uint8_t* ql = blk;
             const uint8_t* qh = blk + 128;
             const int8_t* sc = (const int8_t*)(blk + 192);

@@ -97,6 +97,30 @@ def test_fused_q4_validation():
                          None) == 0
 
 
+def test_kquant_validation():
+    L = dge.lib()
+    # unknown format; cols not a multiple of 256; ldo < cols; odd out address
+    assert L.dequant_f16(4, 4096, 1 << 24, 4, 256, 256, None) == 1
+    assert L.dequant_f16(-1, 4096, 1 << 24, 4, 256, 256, None) == 1
+    assert L.dequant_f16(1, 4096, 1 << 24, 4, 224, 224, None) == 1
+    assert L.dequant_f16(2, 4096, 1 << 24, 4, 256, 255, None) == 1
+    assert L.dequant_f16(2, 4096, (1 << 24) + 1, 4, 256, 256, None) == 1
+    # q overlapping out
+    assert L.dequant_f16(2, 1 << 24, (1 << 24) + 64, 4, 256, 256, None) == 1
+    # q4_0 keeps its own rules (cols % 32, q 2-byte aligned)
+    assert L.dequant_f16(0, 4097, 1 << 24, 4, 64, 64, None) == 1
+    # empty
+    assert L.dequant_f16(1, None, None, 0, 256, 256, None) == 0
+    assert L.dequant_f16(2, None, None, 4, 0, 0, None) == 0
+    # prefill: K must be a multiple of the block width; unknown format
+    assert L.prefill_f16(1, 4, 4, 32, 8, 32, 4096, 1 << 24, 1 << 26, 4, 1, 0, None, None, 0,
+                         None) == 1
+    assert L.prefill_f16(7, 4, 4, 256, 8, 256, 4096, 1 << 24, 1 << 26, 4, 1, 0, None, None, 0,
+                         None) == 1
+    assert L.prefill_f16(2, 0, 4, 256, 8, 256, 4096, 1 << 24, 1 << 26, 4, 1, 0, None, None, 0,
+                         None) == 0
+
+
 def test_workspace_sizes():
     assert dge.gemm_workspace_size_splits(100, 50, 1) == 0
     assert dge.gemm_workspace_size_splits(100, 50, 3) == 3 * 100 * 50 * 4

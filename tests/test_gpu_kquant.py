@@ -1,0 +1,160 @@
+"""GPU parity of the super-block formats (q4_K, q6_K, and q6_K padded to a
+224-byte stride): dequant_f16 bit for bit against the oracle's
+dequantisation, and prefill_f16 (dequant, then the GEMM) against the
+oracle's product of the same binary16 weights.
+
+The dequantisation is integer-like work (a bit pattern out for a bit pattern
+in), so it is compared exactly: every binary16 scale pattern, fully random
+bytes (NaN and infinite scales included, where any NaN matches any NaN),
+ragged and strided outputs and unaligned inputs, and whole prefill weights.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dense_gemm_engineering_amd.binding as dge
+from dense_gemm_engineering_amd import inputs
+from gpu_util import assert_close, bits_of, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BYTES = {"q4_k": 144, "q6_k": 210, "q6_k_224": 224}
+KQ = ["q4_k", "q6_k", "q6_k_224"]
+
+
+def _q(q):
+    return torch.from_numpy(np.ascontiguousarray(q)).cuda()
+
+
+def _same(got, want):
+    """Bitwise equality of binary16 patterns, any NaN matching any NaN."""
+    g, w = got.view(np.float16), want.view(np.float16)
+    return (got == want) | (np.isnan(g) & np.isnan(w))
+
+
+def _check(qtype, q, rows, cols, what=""):
+    got = bits_of(dge.dequant_f16(qtype, _q(q), rows, cols))
+    torch.cuda.synchronize()
+    want = oracle.dequant(qtype, q, rows, cols)
+    ok = _same(got, want)
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError("%s %s: %d weights differ; first at %s: got %04x want %04x"
+                             % (qtype, what, int((~ok).sum()), i, got[i], want[i]))
+
+
+@pytest.mark.parametrize("qtype", KQ)
+def test_random_bytes_bit_exact(qtype):
+    # every byte uniform: all scale patterns, sub-scales, mins and codes
+    r = np.random.Generator(np.random.PCG64(7300 + BYTES[qtype]))
+    rows, cols = 64, 4096
+    q = r.integers(0, 256, size=rows * cols // 256 * BYTES[qtype], dtype=np.uint8)
+    _check(qtype, q, rows, cols, "random bytes")
+
+
+def test_q6_k_every_scale_pattern():
+    r = np.random.Generator(np.random.PCG64(7400))
+    S = 65536
+    q = r.integers(0, 256, size=(S, 210), dtype=np.uint8)
+    d = np.arange(S, dtype=np.uint32).astype(np.uint16)
+    q[:, 208], q[:, 209] = d & 0xFF, d >> 8
+    _check("q6_k", q.reshape(-1), S // 16, 16 * 256, "every d")
+
+
+@pytest.mark.parametrize("field", [0, 2])  # d, dmin
+def test_q4_k_every_scale_pattern(field):
+    r = np.random.Generator(np.random.PCG64(7500 + field))
+    S = 65536
+    q = r.integers(0, 256, size=(S, 144), dtype=np.uint8)
+    other = inputs.to_bits(np.abs(r.standard_normal(S)) * 1e-3, "f16")
+    v = np.arange(S, dtype=np.uint32).astype(np.uint16)
+    q[:, field], q[:, field + 1] = v & 0xFF, v >> 8
+    o = 2 - field
+    q[:, o], q[:, o + 1] = other & 0xFF, other >> 8
+    _check("q4_k", q.reshape(-1), S // 16, 16 * 256, "every %s" % ("d" if field == 0 else "dmin"))
+
+
+@pytest.mark.parametrize("qtype", KQ)
+@pytest.mark.parametrize("rows,cols,pad,qoff,ooff", [
+    (1, 256, 0, 0, 0),      # one super-block
+    (3, 768, 0, 0, 0),      # 9 super-blocks: a ragged last group of 8
+    (5, 512, 8, 0, 0),      # strided rows, 16-byte stores
+    (7, 1280, 3, 0, 0),     # odd ldo: element stores
+    (4, 2304, 0, 1, 0),     # q at an odd address: byte loads
+    (6, 256, 0, 16, 1),     # out not 16-byte aligned
+])
+def test_ragged_strided_unaligned(qtype, rows, cols, pad, qoff, ooff):
+    q = inputs.kquant_weights(qtype, rows, cols, 7, 9)
+    buf = torch.zeros(q.size + qoff, dtype=torch.uint8, device="cuda")
+    buf[qoff:] = _q(q)
+    ldo = cols + pad
+    base = torch.full((rows * ldo + ooff + 8,), -1, dtype=torch.int16, device="cuda")
+    out = base[ooff: ooff + rows * ldo].view(torch.float16).view(rows, ldo)[:, :cols]
+    dge.dequant_f16(qtype, buf[qoff:], rows, cols, out=out)
+    torch.cuda.synchronize()
+    want = oracle.dequant(qtype, q, rows, cols)
+    full = bits_of(base)
+    got = full[ooff: ooff + rows * ldo].reshape(rows, ldo)
+    assert np.array_equal(got[:, :cols], want)
+    # nothing outside the rows x cols window was written
+    assert (got[:, cols:] == 0xFFFF).all()
+    assert (full[:ooff] == 0xFFFF).all() and (full[ooff + rows * ldo:] == 0xFFFF).all()
+
+
+def test_q6_k_padded_layout_matches_the_plain_one():
+    # the same super-blocks at the 224-byte stride, with random padding
+    r = np.random.Generator(np.random.PCG64(7700))
+    rows, cols = 40, 2048
+    q = inputs.kquant_weights("q6_k", rows, cols, 7, 12)
+    S = q.size // 210
+    padded = r.integers(0, 256, (S, 224), dtype=np.uint8)
+    padded[:, :210] = q.reshape(S, 210)
+    a = bits_of(dge.dequant_f16("q6_k", _q(q), rows, cols))
+    b = bits_of(dge.dequant_f16("q6_k_224", _q(padded.reshape(-1)), rows, cols))
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, oracle.dequant("q6_k", q, rows, cols))
+
+
+def test_q4_0_through_the_generic_entry_point():
+    q = inputs.q4_weights(96, 512, 4, 7)
+    a = bits_of(dge.dequant_f16("q4_0", _q(q), 96, 512))
+    b = bits_of(dge.dequant_q4_f16(_q(q), 96, 512))
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, oracle.dequant_q4(q, 96, 512))
+
+
+@pytest.mark.parametrize("qtype,shape", [(t, s) for t in ("q4_k", "q6_k")
+                                          for s in ("up", "attn", "down")] + [("q6_k_224", "attn")])
+def test_prefill_full_size(qtype, shape):
+    A, q, N, K = inputs.kquant_projection(qtype, shape)
+    dA = to_dev(A, "f16")
+    n = dge.gemm_workspace_size(2048, N, K, torch.float16)
+    ws = torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda") if n else None
+    w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    C = dge.prefill_f16(qtype, dA, _q(q), N, K, w16=w16, workspace=ws)
+    torch.cuda.synchronize()
+    W16 = oracle.dequant(qtype, q, N, K)
+    assert np.array_equal(bits_of(w16), W16), "whole weight, bit for bit"
+    rows = sample_rows(2048, 16, seed=N + K + BYTES[qtype])
+    T, U = oracle.gemm(A[rows], W16, "f16", trans_b=True)
+    assert_close(C[torch.from_numpy(rows).cuda()], T, U, what="%s %s" % (qtype, shape))
+
+
+@pytest.mark.parametrize("qtype", KQ)
+def test_prefill_tail_shape_and_bias_gelu(qtype):
+    # tails in M and N (33 tokens, 70 outputs), the smallest K
+    M, N, K = 33, 70, 256
+    r = np.random.Generator(np.random.PCG64(7600))
+    A = inputs.to_bits(r.normal(0, 1, (M, K)), "f16")
+    q = inputs.kquant_weights(qtype, N, K, 7, 11)
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), "f16")
+    bias = oracle.decode(bias_bits, "f16")
+    C = dge.prefill_f16(qtype, to_dev(A, "f16"), _q(q), N, K, out_dtype=torch.float32,
+                        epi="bias_gelu", bias=to_dev(bias_bits, "f16"))
+    torch.cuda.synchronize()
+    T, U = oracle.gemm(A, oracle.dequant(qtype, q, N, K), "f16", trans_b=True, epi="bias_gelu",
+                       bias=bias)
+    assert_close(C, T, U, bias=bias)

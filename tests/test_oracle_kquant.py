@@ -147,6 +147,21 @@ def test_q6_k_every_scale_pattern():
     assert same.all()
 
 
+def test_q6_k_padded_stride_ignores_the_padding():
+    # the same super-blocks at a 224-byte stride, 14 random bytes after each
+    r = np.random.Generator(np.random.PCG64(7200))
+    S = 12
+    q = _pack_q6_k(np.abs(r.normal(0, 0.01, S)).astype(np.float16).view(np.uint16),
+                   r.integers(-128, 128, (S, 16)), r.integers(0, 64, (S, 256)))
+    padded = r.integers(0, 256, (S, 224), dtype=np.uint8)
+    padded[:, :210] = q.reshape(S, 210)
+    want = oracle.dequant("q6_k", q, 3, 4 * 256)
+    assert np.array_equal(oracle.dequant("q6_k_224", padded.reshape(-1), 3, 4 * 256), want)
+    # the padding really is skipped: shifting it into a block changes the result
+    assert not np.array_equal(oracle.dequant("q6_k", padded.reshape(-1)[: S * 210], 3, 4 * 256),
+                              want)
+
+
 def test_shapes_rejected():
     import pytest
     with pytest.raises(ValueError):
