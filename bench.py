@@ -229,6 +229,30 @@ def bench_kquant(dge, inputs, torch, steps, prefill, rotate_bytes=300e6):
     return out
 
 
+def bench_streamk(dge, inputs, torch, steps):
+    """The persistent schedule with a stream-K tail (algo "streamk", tile
+    chosen by its model) beside the default schedule, fp16 N x K weights."""
+    out = {}
+    shapes = {"square_4096": (4096, 4096, 4096), "up": (2048, 11008, 4096),
+              "attn": (2048, 4096, 4096), "down": (2048, 4096, 11008)}
+    for name, (M, N, K) in shapes.items():
+        A = torch.randn(M, K, device="cuda", dtype=torch.float16) / K ** 0.5
+        B = torch.randn(N, K, device="cuda", dtype=torch.float16) / K ** 0.5
+        C = torch.empty(M, N, device="cuda", dtype=torch.float16)
+        n = max(dge.gemm_workspace_size(M, N, K, torch.float16),
+                dge.gemm_workspace_size_streamk(M, N, K))
+        ws = torch.empty(n // 4 + 1, dtype=torch.float32, device="cuda")
+        td, _ = time_launches(lambda: dge.gemm_f16(A, B, C, trans_b=True, workspace=ws), steps, 3,
+                              torch)
+        ts, _ = time_launches(lambda: dge.gemm_ex(A, B, C, trans_b=True, workspace=ws,
+                                                  algo="streamk"), steps, 3, torch)
+        out[name] = {"default_us": td * 1e6, "streamk_us": ts * 1e6,
+                     "default_TFLOPs": gemm_flops(M, N, K) / td / 1e12,
+                     "streamk_TFLOPs": gemm_flops(M, N, K) / ts / 1e12}
+        del A, B, C, ws
+    return out
+
+
 def bench_decode(dge, inputs, torch, steps, rotate_bytes=300e6):
     """The decode shape: M input rows against one 4096 x 4096 fp16 weight
     (HBM-cold by rotating weight copies); bound by reading W once."""
@@ -389,6 +413,7 @@ def main():
         line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps)
         line["prefill_kquant"] = bench_kquant(dge, inputs, torch, extra_steps,
                                               line["prefill_2048"])
+        line["streamk_vs_default"] = bench_streamk(dge, inputs, torch, extra_steps)
         line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps)
         line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps)
         line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)

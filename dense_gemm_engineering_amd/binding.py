@@ -19,14 +19,15 @@ EPI = {"none": 0, "bias": 1, "bias_gelu": 2}
 OUT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 IN = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
 ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "mfma": 3, "mfma_direct": 4, "skinny": 5,
-        "decode": 6}
+        "decode": 6, "streamk": 7}
 TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x256w8": 5}
 QTYPE = {"q4_0": 0, "q4_k": 1, "q6_k": 2, "q6_k_224": 3}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "dequant_q4_f16", "prefill_q4_f16",
            "gemm_q4_f16", "dequant_f16", "prefill_f16",
-           "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_status_string", "gemm_init")
+           "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_workspace_size_streamk",
+           "gemm_status_string", "gemm_init")
 
 
 class GemmError(RuntimeError):
@@ -76,6 +77,8 @@ def lib():
         L.gemm_workspace_size.restype = sz
         L.gemm_workspace_size_splits.argtypes = [i64, i64, i32]
         L.gemm_workspace_size_splits.restype = sz
+        L.gemm_workspace_size_streamk.argtypes = [i64, i64, i64, i32]
+        L.gemm_workspace_size_streamk.restype = sz
         L.gemm_status_string.argtypes = [i32]
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_init.argtypes = []
@@ -249,6 +252,10 @@ def gemm_workspace_size(M, N, K, dtype=torch.float16):
 
 def gemm_workspace_size_splits(M, N, splits):
     return lib().gemm_workspace_size_splits(M, N, splits)
+
+
+def gemm_workspace_size_streamk(M, N, K, tile="auto"):
+    return lib().gemm_workspace_size_streamk(M, N, K, TILE[tile])
 
 
 def gemm_init():

@@ -212,19 +212,84 @@ double schedule_us(int64_t M, int64_t N, int64_t K, int tile, int splits, int bk
     return us;
 }
 
+// Persistent schedule with a stream-K tail (direct-to-LDS kernels): the grid
+// is every CU slot the tile allows (at most one workgroup per iteration).
+// Its time is R whole-tile rounds plus the tail's ceil(I / G) stages, plus
+// per extra segment a share of the prologue and epilogue the overlap does
+// not hide, plus, when tail tiles are split, the fp32 partial stores and the
+// reduction (measured on MI355X: ~45 us per launch for 256 x 256 tiles,
+// scaling with the tile area).
+constexpr double kSkSegmentUs = 3.0, kSkPartialUs = 45.0;
+
+int64_t sk_grid(int tile, int64_t iters, int cus) {
+    return std::min<int64_t>((int64_t)cus * tile_occupancy(tile), iters);
+}
+
+// Whole-tile rounds before the stream-K tail: as many full rounds of the
+// grid as fit, less one while the tail would have fewer iterations than
+// workgroups (every workgroup's tail range must be non-empty, or a split
+// tile would count a workgroup that never arrives).
+int64_t sk_rounds(int64_t tiles, int64_t S, int64_t G) {
+    int64_t R = tiles / G;
+    while (R > 0 && tiles > R * G && (tiles - R * G) * S < G) --R;
+    return R;
+}
+
+// Workspace of the stream-K schedule: 2 fp32 partial tiles per workgroup,
+// then one 32-bit counter per tile (256-byte aligned).
+size_t sk_counter_offset(int tile, int64_t grid) {
+    const TileShape ts = tile_shape(tile);
+    return (size_t)2 * grid * ts.bm * ts.bn * sizeof(float);
+}
+size_t sk_ws_bytes(int tile, int64_t grid, int64_t tiles) {
+    return sk_counter_offset(tile, grid) + ((size_t)tiles * 4 + 255) / 256 * 256;
+}
+
+double sk_schedule_us(int64_t M, int64_t N, int64_t K, int tile, int bk, int cus) {
+    const TileShape ts = tile_shape(tile);
+    const TileCost c = tile_cost(tile);
+    const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+    const int64_t S = ceil_div(K, bk), G = sk_grid(tile, tiles * S, cus);
+    const int64_t R = sk_rounds(tiles, S, G), I = (tiles - R * G) * S;
+    const int64_t per = I > 0 ? (I + G - 1) / G : 0;  // tail stages per workgroup
+    double us = c.fixed_us + c.us_per_k * (double)((R * S + per) * bk);
+    const int64_t segments = R + (per + S - 1) / S + (I % G != 0 ? 1 : 0);
+    us += kSkSegmentUs * (double)std::max<int64_t>(segments - 1, 0);
+    if (I > 0 && (I % G != 0 || (I / G) % S != 0))
+        us += kSkPartialUs * (double)(ts.bm * ts.bn) / 65536.0;
+    return us;
+}
+
 // Joint choice of tile shape and K split.  tile / splits: the caller's
 // request (GEMM_TILE_AUTO / 0 = free); allowed: bit t set for each tile id
 // that may be chosen.  A split is only considered while ws_bytes covers its
 // partials; each K slice keeps at least 16 stages.
+// sk_allowed: bit t set where the stream-K schedule may run tile t; with
+// sk_only, only those are considered.  *sk = 1 when stream-K wins.
 void choose_schedule(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
-                     int* tile, int* splits, unsigned allowed = ~0u) {
+                     int* tile, int* splits, unsigned allowed = ~0u, unsigned sk_allowed = 0,
+                     bool sk_only = false, int* sk = nullptr) {
     const int bk = stage_k(dt);
     const int t_lo = *tile == GEMM_TILE_AUTO ? TILE_256x256 : *tile;
     const int t_hi = *tile == GEMM_TILE_AUTO ? TILE_LAST : *tile;
-    int best_t = t_lo, best_s = 1;
+    int best_t = t_lo, best_s = 1, best_sk = 0;
     double best = 1e300;
     for (int t = t_lo; t <= t_hi; ++t) {
-        if (!(allowed >> t & 1u)) continue;
+        if ((sk_allowed >> t & 1u) && *splits <= 1) {
+            const TileShape ts = tile_shape(t);
+            const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+            const int64_t I = tiles * ceil_div(K, bk);
+            if (ws_bytes >= sk_ws_bytes(t, sk_grid(t, I, cus), tiles)) {
+                const double us = sk_schedule_us(M, N, K, t, bk, cus);
+                if (us < best * 0.999) {
+                    best = us;
+                    best_t = t;
+                    best_s = 1;
+                    best_sk = 1;
+                }
+            }
+        }
+        if (sk_only || !(allowed >> t & 1u)) continue;
         for (int sp = 1; sp <= 8; ++sp) {
             if (*splits > 0 && sp != *splits) continue;
             if (sp > 1 && (K / sp < 16 * (int64_t)bk || ws_bytes < ws_bytes_for(M, N, sp)))
@@ -234,11 +299,13 @@ void choose_schedule(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws
                 best = us;
                 best_t = t;
                 best_s = sp;
+                best_sk = 0;
             }
         }
     }
     *tile = best_t;
     if (*splits == 0) *splits = best_s;
+    if (sk) *sk = best_sk;
 }
 
 size_t ws_bytes_for(int64_t M, int64_t N, int splits) {
@@ -252,7 +319,27 @@ gemm_status_t launch_status(hipError_t e) {
 
 // direct: 0 = register-staged kernel only, 1 = direct-to-LDS kernel when the
 // problem qualifies (full tiles, 16-bit inputs, aligned operands).
-gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct) {
+// Tiles whose stream-K schedule can run this problem: the direct-to-LDS
+// kernel's conditions (16-bit inputs, full tiles, whole stages, aligned
+// operands, and for a K x N B at least 128 columns).
+unsigned streamk_tiles(const Gemm& g) {
+    if (g.b_q4 || g.dt == IN_F32 || g.K <= 0 || g.K % stage_k(g.dt) != 0) return 0;
+    if (env_int("GEMM_DIRECT", 1) == 0 || env_int("GEMM_STREAMK", 1) == 0) return 0;
+    const int vec_el = 16 / in_bytes(g.dt);
+    const bool vec = aligned16(g.A) && aligned16(g.B) && aligned16(g.C) && g.lda % vec_el == 0 &&
+                     g.ldb % vec_el == 0 && (g.ldc * out_bytes(g.c_type)) % 16 == 0;
+    if (!vec) return 0;
+    unsigned m = 0;
+    for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
+        const TileShape s = tile_shape(t);
+        if (g.M % s.bm == 0 && g.N % s.bn == 0 && (g.trans_b || s.bn >= 128)) m |= 1u << t;
+    }
+    return m;
+}
+
+// streamk: 1 = the stream-K schedule was asked for (it runs where eligible)
+gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
+                       int streamk = 0) {
     if (tile != GEMM_TILE_AUTO && (tile < TILE_256x256 || tile > TILE_LAST))
         return GEMM_ERR_INVALID_VALUE;
     const bool explicit_split = splits > 1;
@@ -270,8 +357,19 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
                         aligned16(g.C) && g.lda % 8 == 0 && (g.ldc * out_bytes(g.c_type)) % 16 == 0;
         if (!ok) return GEMM_ERR_NOT_SUPPORTED;
     }
-    if (tile == GEMM_TILE_AUTO || splits == 0)
-        choose_schedule(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, &tile, &splits, allowed);
+    // the stream-K schedule only runs when asked for: measured on MI355X it
+    // does not beat the data-parallel and split schedules on any workload
+    // here (the workgroups of an XCD sit at different K stages, so its 4 MB
+    // L2 no longer shares A/B stage blocks between them; split tiles move
+    // BM x BN fp32 partials through memory twice)
+    unsigned sk_allowed = direct && streamk ? streamk_tiles(g) : 0;
+    if (tile != GEMM_TILE_AUTO) sk_allowed &= 1u << tile;
+    const bool sk_only = streamk && sk_allowed != 0;
+    int sk = 0;
+    if (tile == GEMM_TILE_AUTO || splits == 0 || sk_only)
+        choose_schedule(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, &tile, &splits, allowed,
+                        sk_allowed, sk_only, &sk);
+    if (sk_only && !sk) return GEMM_ERR_WORKSPACE;  // stream-K was asked for and does not fit
     const TileShape ts = tile_shape(tile);
     const int bk = stage_k(g.dt);
     const int max_splits = std::max(1, ceil_div(g.K, bk));
@@ -327,9 +425,28 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct)
     }
     const bool use_direct = direct && fast && g.dt != IN_F32 &&
                             (g.trans_b || ts.bn >= 128) && env_int("GEMM_DIRECT", 1) != 0;
+    if (sk && use_direct && aligned16(g.ws)) {
+        const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n, S = g.K / bk;
+        const int64_t G = sk_grid(tile, tiles * S, cus);
+        a.ws = nullptr;
+        a.splits = 1;
+        a.k_per_split = (int)g.K;
+        a.sk_stages = (int)S;
+        a.sk_rounds = (int)sk_rounds(tiles, S, G);
+        a.sk_ws = (float*)g.ws;
+        a.sk_cnt = (unsigned*)((char*)g.ws + sk_counter_offset(tile, G));
+        // the arrival counters are only read when a tail tile is split
+        const int64_t I = (tiles - (int64_t)a.sk_rounds * G) * S;
+        const bool split_tail = I > 0 && (I % G != 0 || (I / G) % S != 0);
+        e = split_tail ? launch_clear_u32(a.sk_cnt, tiles, g.stream) : hipSuccess;
+        if (e == hipSuccess)
+            e = g.dt == IN_F16 ? launch_mfma_direct_f16(tile, g.trans_b, a, (int)G, 1, g.stream)
+                               : launch_mfma_direct_bf16(tile, g.trans_b, a, (int)G, 1, g.stream);
+        return launch_status(e);
+    }
     if (use_direct) {
-        e = g.dt == IN_F16 ? launch_mfma_direct_f16(tile, g.trans_b, a, (int)nwg, g.stream)
-                           : launch_mfma_direct_bf16(tile, g.trans_b, a, (int)nwg, g.stream);
+        e = g.dt == IN_F16 ? launch_mfma_direct_f16(tile, g.trans_b, a, (int)nwg, 0, g.stream)
+                           : launch_mfma_direct_bf16(tile, g.trans_b, a, (int)nwg, 0, g.stream);
         if (e != hipSuccess) return launch_status(e);
         if (splits > 1)
             e = launch_splitk_fixup(g.dt, simple_args(g), (const float*)g.ws, splits, g.stream);
@@ -408,7 +525,7 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
     if (st != GEMM_OK) return st;
     gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
     if (tuning) tn = *tuning;
-    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_DECODE) return GEMM_ERR_INVALID_VALUE;
+    if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_STREAMK) return GEMM_ERR_INVALID_VALUE;
     if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8) return GEMM_ERR_INVALID_VALUE;
     if (tn.splits < 0) return GEMM_ERR_INVALID_VALUE;
     if (g.M == 0 || g.N == 0) return GEMM_OK;
@@ -432,6 +549,9 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
             if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
             if (g.K > 0 && decode_eligible(g)) return run_decode(g);
             return run_mfma(g, tn.tile, 1, dev.cus, 1);
+        case GEMM_ALGO_STREAMK:
+            if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
+            return run_mfma(g, tn.tile, 0, dev.cus, 1, 1);
         case GEMM_ALGO_AUTO:
             if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && g.K > 0 && decode_eligible(g))
                 return run_decode(g);
@@ -653,6 +773,21 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {
     int tile = GEMM_TILE_AUTO, s = 0;
     choose_schedule(M, N, K, dtype, dev.cus, (size_t)-1, &tile, &s);
     return ws_bytes_for(M, N, s);
+}
+
+size_t gemm_workspace_size_streamk(int64_t M, int64_t N, int64_t K, int tile) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    if (tile != GEMM_TILE_AUTO && (tile < TILE_256x256 || tile > TILE_LAST)) return 0;
+    DeviceInfo dev{1, 256};
+    if (current_device(&dev) != GEMM_OK) dev.cus = 256;
+    size_t need = 0;
+    for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
+        if (tile != GEMM_TILE_AUTO && t != tile) continue;
+        const TileShape ts = tile_shape(t);
+        const int64_t tiles = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+        need = std::max(need, sk_ws_bytes(t, sk_grid(t, tiles * ceil_div(K, 64), dev.cus), tiles));
+    }
+    return need;
 }
 
 size_t gemm_workspace_size_splits(int64_t M, int64_t N, int splits) {

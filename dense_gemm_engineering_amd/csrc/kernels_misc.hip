@@ -55,6 +55,19 @@ hipError_t launch_splitk_fixup(int dt, const SimpleArgs& a, const float* ws, int
     }
 }
 
+__global__ __launch_bounds__(256) void clear_u32_kernel(unsigned* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+hipError_t launch_clear_u32(unsigned* p, int64_t n, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
                              int vec_out, hipStream_t s) {
     const int64_t total = rows * (cols / 32);

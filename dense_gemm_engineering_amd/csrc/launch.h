@@ -44,8 +44,11 @@ hipError_t launch_mfma_f32(int tile, int trans_b, int fast, const MfmaArgs& a, i
 
 // Direct-to-LDS variant (16-bit inputs, full tiles, 16-byte aligned operands).
 // Returns hipErrorInvalidValue for a tile it does not provide.
-hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, hipStream_t s);
-hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg,
+// sk = 1: the persistent stream-K schedule, nwg = its grid (a.sk_* set, the
+// arrival counters zeroed on the same stream first).
+hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, int sk,
+                                  hipStream_t s);
+hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg, int sk,
                                    hipStream_t s);
 // Fused q4-weight GEMM (p.B = q4 blocks of an N x K weight, 4-byte aligned;
 // K % 64 == 0; full tiles of the given shape only).
@@ -64,6 +67,8 @@ hipError_t launch_decode(int dt, const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s);
 hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s);
+// n 32-bit zeros at p (a fill kernel: no memset node if the stream is captured).
+hipError_t launch_clear_u32(unsigned* p, int64_t n, hipStream_t s);
 hipError_t launch_splitk_fixup(int dt, const SimpleArgs& a, const float* ws, int splits,
                                hipStream_t s);
 hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,

@@ -157,11 +157,13 @@ __device__ inline void q4_decode4(uint32_t nib, h2v d2, uint32_t* o) {
     o[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2v, v23) - off) * d2);
 }
 
-template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS, bool Q4 = false>
+template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS, bool Q4 = false,
+          bool SK = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p) {
     static_assert(DT == IN_F16 || DT == IN_BF16, "16-bit inputs only");
     static_assert(MS == 16 || MS == 32, "MFMA block size");
     static_assert(!Q4 || (TRANS_B && DT == IN_F16), "q4 weights are N x K, with fp16 A");
+    static_assert(!(SK && Q4), "the stream-K schedule runs the 16-bit B path");
     constexpr int NW = WM * WN;
     constexpr int BK = 64;
     constexpr int KBLK = 512 / MS;   // k per k-block: 32 (16x16x32) or 16 (32x32x16)
@@ -178,51 +180,50 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int CPR_B = BN / 8;             // 16-byte chunks per k-row of a K x N B tile
     constexpr int RPI_B = 1024 / (BN * 2);    // k-rows per 1 KB direct-load instruction
     static_assert(TRANS_B || RPI_B * BN * 2 == 1024, "whole k-rows per instruction");
-    static_assert(NW * MS * (WTN + 8) * 4 <= 2 * (A_BYTES + B_BYTES), "epilogue staging fits");
+    // epilogue staging (from buffer 0 on): one MS-row strip per wave
+    constexpr int STG_BYTES = NW * MS * (WTN + (MS == 32 ? 8 : 4)) * 4;
+    static_assert(STG_BYTES <= 2 * (A_BYTES + B_BYTES), "epilogue staging fits");
+    // stream-K: the next tile's first stage can load into buffer 1 during the
+    // epilogue only where the staging stays inside buffer 0
+    constexpr bool SK_PREFETCH = STG_BYTES <= A_BYTES + B_BYTES;
 
     __shared__ __attribute__((aligned(1024))) char lds[2][A_BYTES + B_BYTES];
+    __shared__ int sk_flag;  // stream-K: a counter value broadcast to the workgroup
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
-
-    const int ntiles = p.tiles_m * p.tiles_n;
-    const int lin = remap_xcd(blockIdx.x, ntiles * p.splits);
-    const int split = lin / ntiles;
-    int tm, tn;
-    grouped_tile(lin % ntiles, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int kbeg = split * p.k_per_split;
-    const int kend = min(kbeg + p.k_per_split, p.K);
-    const int nk = (kend - kbeg) / BK;
 
     // ---- per-lane global source offsets (elements) for the direct loads
     // A: instruction i of this wave fills rows 8 * (wave * IA + i) + lane / 8;
     // its chunk swizzle depends on the row block, so it is applied per instruction
     const int a_row = 8 * wave * IA + (lane >> 3);
     const int k_lane_chunk = lane & 7;
-    const uint16_t* a_src = (const uint16_t*)p.A + (int64_t)(m0 + a_row) * p.lda + kbeg;
     const int64_t a_step = (int64_t)8 * p.lda;  // next instruction: 8 rows down
-    const uint16_t* b_src;
-    int64_t b_step;
-    if constexpr (TRANS_B) {
-        const int b_row = 8 * wave * IB + (lane >> 3);
-        b_src = (const uint16_t*)p.B + (int64_t)(n0 + b_row) * p.ldb + kbeg;
-        b_step = (int64_t)8 * p.ldb;
-    } else {
-        // instruction i fills k-rows RPI * (wave * IB + i) + lane / CPR; the
-        // chunk swizzle depends on the k-row, so it is applied per instruction
-        const int krow = RPI_B * wave * IB + lane / CPR_B;
-        b_src = (const uint16_t*)p.B + (int64_t)(kbeg + krow) * p.ldb + n0;
-        b_step = (int64_t)RPI_B * p.ldb;
-    }
+    // B (K x N): instruction i fills k-rows RPI * (wave * IB + i) + lane / CPR;
+    // the chunk swizzle depends on the k-row, so it is applied per instruction
+    const int64_t b_step = TRANS_B ? (int64_t)8 * p.ldb : (int64_t)RPI_B * p.ldb;
+    // the current tile: origin (m0, n0), first k kbeg, and the sources there
+    int m0 = 0, n0 = 0, kbeg = 0;
+    const uint16_t* a_src = nullptr;
+    const uint16_t* b_src = nullptr;
+    auto start_tile = [&](int tm0, int tn0, int tk0) __attribute__((always_inline)) {
+        m0 = tm0;
+        n0 = tn0;
+        kbeg = tk0;
+        a_src = (const uint16_t*)p.A + (int64_t)(m0 + a_row) * p.lda + kbeg;
+        if constexpr (TRANS_B)
+            b_src = (const uint16_t*)p.B + (int64_t)(n0 + 8 * wave * IB + (lane >> 3)) * p.ldb + kbeg;
+        else
+            b_src = (const uint16_t*)p.B + (int64_t)(kbeg + RPI_B * wave * IB + lane / CPR_B) * p.ldb + n0;
+    };
     const int b_lane_chunk = lane % CPR_B;
     const int b_krow0 = RPI_B * wave * IB + lane / CPR_B;
     const int64_t a_kstep = BK;                                        // A per stage
     const int64_t b_kstep = TRANS_B ? (int64_t)BK : (int64_t)BK * p.ldb;  // B per stage
 
     // Direct loads [lo, hi) of the IA + IB of stage kt, into buffer st.
-    auto issue_part = [&](int st, int kt, int lo, int hi) {
+    auto issue_part = [&](int st, int kt, int lo, int hi) __attribute__((always_inline)) {
         DGE_LDS char* la = (DGE_LDS char*)&lds[st][0] + wave * IA * 1024;
         DGE_LDS char* lb = (DGE_LDS char*)&lds[st][A_BYTES] + wave * IB * 1024;
         const uint16_t* ga = a_src + kt * a_kstep;
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     static_assert(!Q4 || (2 * BN) % NTHR == 0 || 2 * BN < NTHR, "q4 task split");
     uint32_t qraw[QT][5];
     const int64_t qnb = p.K / 32;  // blocks per weight row (even: K % 64 == 0)
-    auto q4_load = [&](int kt) {
+    auto q4_load = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < QT; ++i) {
             const int t = tid + i * NTHR;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             for (int e = 0; e < 5; ++e) qraw[i][e] = src[e];
         }
     };
-    auto q4_store = [&](int st) {
+    auto q4_store = [&](int st) __attribute__((always_inline)) {
         DGE_LDS char* lb = (DGE_LDS char*)&lds[st][A_BYTES];
 #pragma unroll
         for (int i = 0; i < QT; ++i) {
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // ---- fragment reads of k-block kb
     // A (and K-contiguous B): row r = base + (lane % MS), chunk
     // (CPK kb + lane / MS) ^ swz_k(r) (the same swizzle for every block of rows).
-    auto read_rows = [&](const DGE_LDS char* base, int row0, int kb, int ntile, u32x4* f) {
+    auto read_rows = [&](const DGE_LDS char* base, int row0, int kb, int ntile, u32x4* f) __attribute__((always_inline)) {
         const int r = row0 + (lane % MS);
         const DGE_LDS char* q = base + r * 128 + (((kb * CPK + lane / MS) ^ swz_k<MS>(r)) << 4);
 #pragma unroll
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // K x N B via transposed reads.  Lane group g = lane / 16 covers k-rows
     // kb KBLK + 8 (g / (MS / 16)) + 4 h + (t / 4) and columns
     // wn0 + MS j + 16 (g % (MS / 16)) + 4 (t % 4).
-    auto read_bt = [&](const DGE_LDS char* base, int kb, u32x4* f) {
+    auto read_bt = [&](const DGE_LDS char* base, int kb, u32x4* f) __attribute__((always_inline)) {
         const int t = lane & 15, g = lane >> 4;
         const int kofs = MS == 16 ? 8 * g : 8 * (g >> 1);
         const int nofs = MS == 16 ? 0 : 16 * (g & 1);
@@ -328,15 +329,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     typedef typename AccBlock<MS>::T Acc;
     constexpr int NACC = MS * MS / 64;  // accumulator elements per lane per block
     Acc acc[TM][TN];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.f;
+                for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.f;
+    };
 
     u32x4 fa[2][TM], fb[2][TN];
-    auto read_kblock = [&](int st, int kb, u32x4* a, u32x4* b) {
+    auto read_kblock = [&](int st, int kb, u32x4* a, u32x4* b) __attribute__((always_inline)) {
         const DGE_LDS char* la = (const DGE_LDS char*)&lds[st][0];
         const DGE_LDS char* lb = (const DGE_LDS char*)&lds[st][A_BYTES];
         read_rows(la, wm0, kb, TM, a);
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             read_bt(lb, kb, b);
     };
     // MFMAs [lo, hi) of one k-block, row-major over the TM x TN blocks.
-    auto mma_range = [&](const u32x4* a, const u32x4* b, int lo, int hi) {
+    auto mma_range = [&](const u32x4* a, const u32x4* b, int lo, int hi) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < TM * TN; ++x)
             if (x >= lo && x < hi) {
@@ -372,15 +375,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int NP0 = NDMA / DPART;                    // loads in the first part
     constexpr int TAIL = NMF / (MS == 16 ? 4 : 2) > 0 ? NMF / (MS == 16 ? 4 : 2) : 1;  // after the barrier
 
+    // Main loop over the nk stages of the current tile, stage kt in buffer
+    // (kt + par) & 1; pre: stage 0's loads into buffer par are already in
+    // flight.  Ends with every load landed and both buffers free.
     // Prologue: stages 0 and 1 in flight, wait for stage 0, read its k-block 0.
-    issue_part(0, 0, 0, NDMA);
+    auto mainloop = [&](int nk, int par, bool pre) __attribute__((always_inline)) {
+    if (!pre) issue_part(par, 0, 0, NDMA);
     if constexpr (Q4) q4_load(0);
-    issue_part(1, nk > 1 ? 1 : 0, 0, NP0);
-    if constexpr (Q4) q4_store(0);
+    issue_part(par ^ 1, nk > 1 ? 1 : 0, 0, NP0);
+    if constexpr (Q4) q4_store(par);
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((NP0 & 15) | ((NP0 >> 4) << 14)));  // vmcnt(NP0)
     __syncthreads();
     if constexpr (Q4) q4_load(nk > 1 ? 1 : 0);
-    read_kblock(0, 0, fa[0], fb[0]);
+    read_kblock(par, 0, fa[0], fb[0]);
 
     // Steady state, stage kt (buffer kt & 1), k-blocks 0 .. KB-1 with their
     // fragments alternating between two register sets:
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // Past the last stage the loads re-fetch the last stage (never read) so
     // the body has no branch and the scheduling groups cover all of it.
     for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
+        const int st = (kt + par) & 1;
 #pragma unroll
         for (int kb = 0; kb < KB - 1; ++kb) {
             read_kblock(st, kb + 1, fa[(kb + 1) & 1], fb[(kb + 1) & 1]);
@@ -436,10 +443,191 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if constexpr (MS == 32)
-        epilogue_tile32<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], m0, n0, split);
-    else
-        epilogue_tile<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], m0, n0, split);
+    };
+
+    // the fused epilogue of tile (em0, en0), staged through buffer 0
+    auto epilogue = [&](int em0, int en0, int split) __attribute__((always_inline)) {
+        if constexpr (MS == 32)
+            epilogue_tile32<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], em0, en0, split);
+        else
+            epilogue_tile<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], em0, en0, split);
+    };
+
+    if constexpr (!SK) {
+        // one (tile, K slice) per workgroup
+        const int ntiles = p.tiles_m * p.tiles_n;
+        const int lin = remap_xcd(blockIdx.x, ntiles * p.splits);
+        const int split = lin / ntiles;
+        int tm, tn;
+        grouped_tile(lin % ntiles, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+        const int k0 = split * p.k_per_split;
+        start_tile(tm * BM, tn * BN, k0);
+        zero_acc();
+        mainloop((min(k0 + p.k_per_split, p.K) - k0) / BK, 0, false);
+        epilogue(m0, n0, split);
+    } else {
+        // Persistent schedule over the grid's G workgroups: first R rounds of
+        // whole tiles, round r giving tile r G + v to workgroup v (so the
+        // tiles running at once are consecutive in the grouped order and sit
+        // at the same K stage, as in a data-parallel launch); then stream-K
+        // over the T - R G tail tiles: their I = (T - R G) x S (tile, stage)
+        // iterations split into equal contiguous ranges, consecutive ranges
+        // on one XCD.  A range covers at most a partial tile at each end and
+        // whole tiles between.  A whole tile ends with the fused epilogue.  A partial segment stores
+        // its fp32 accumulators in a slot of the workspace and counts itself
+        // in the tile's counter; the segment that completes the count sums all
+        // segments of the tile in k order (bitwise the same sum whichever
+        // segment finishes) and runs the epilogue.  No workgroup ever waits
+        // for another.  Between segments, the next tile's first stage is
+        // loaded into buffer 1 while the epilogue stages through buffer 0
+        // (tiles whose staging fits in buffer 0: 256 x 256 with 8 waves,
+        // 256 x 128 and 128 x 64).
+        const int G = gridDim.x;
+        const int v = remap_xcd(blockIdx.x, G);
+        const int S = p.sk_stages;
+        const int R = p.sk_rounds, TB = R * G;  // whole-tile rounds; first tail tile
+        const int64_t I = (int64_t)(p.tiles_m * p.tiles_n - TB) * S;
+        auto it_of = [&](int w) __attribute__((always_inline)) { return (int64_t)w * I / G; };
+        constexpr int CH = TM * TN * NACC / 4;  // 16-byte accumulator chunks per lane
+        // slot of workgroup w's partial of the tile starting at iteration x:
+        // 0 if it is the first segment of w's range, 1 if the last
+        auto slot = [&](int w, int64_t x) __attribute__((always_inline)) {
+            return p.sk_ws + (int64_t)(2 * w + (it_of(w) >= x ? 0 : 1)) * (BM * BN);
+        };
+        // chunk c of the lane's accumulators: elements 4 (c % Q) .. + 3 of
+        // block c / Q, Q = NACC / 4 (indices are compile-time after unrolling)
+        constexpr int Q = NACC / 4;
+        auto get_chunk = [&](const Acc (&a)[TM][TN], int c) {
+            const Acc& b = a[(c / Q) / TN][(c / Q) % TN];
+            const int e = 4 * (c % Q);
+            return (f32x4){b[e], b[e + 1], b[e + 2], b[e + 3]};
+        };
+        auto set_chunk = [&](Acc (&a)[TM][TN], int c, const f32x4& y) {
+            Acc& b = a[(c / Q) / TN][(c / Q) % TN];
+            const int e = 4 * (c % Q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[e + r] = y[r];
+        };
+        auto finish = [&](int tile, int ks, int ke, int em0, int en0) __attribute__((always_inline)) {
+            if (ks == 0 && ke == S) {
+                epilogue(em0, en0, 0);
+                return;
+            }
+            const int64_t x = (int64_t)(tile - TB) * S;     // the tile's first tail iteration
+            const int w0 = (int)(((x + 1) * G - 1) / I);  // owner of the tile's first stage
+            const int nseg = (int)(((x + S) * G - 1) / I) - w0 + 1;
+            const int j = v - w0;
+            bool write = true;
+            if (j == 0) {
+                // the first segment usually finishes last (it closes its
+                // workgroup's range): if every other one has counted itself,
+                // finish without storing
+                if (tid == 0)
+                    sk_flag = (int)__hip_atomic_load(&p.sk_cnt[tile], __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                write = sk_flag != nseg - 1;
+                __syncthreads();
+            }
+            if (write) {
+                // device-scope stores write through this XCD's L2; waiting
+                // for them puts the partial at device scope before the count
+                // (an agent-scope fence would write back and invalidate the
+                // whole L2 instead, for every partial)
+                // slot layout: element e of chunk c of thread t at (4 c + e) x
+                // threads + t, so each store covers 256 contiguous bytes
+                float* dst = slot(v, x) + tid;
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const f32x4 y = get_chunk(acc, c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __hip_atomic_store(dst + (4 * c + e) * NW * 64, y[e], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                __syncthreads();
+                if (tid == 0) sk_flag = (int)atomicAdd(&p.sk_cnt[tile], 1u);
+                __syncthreads();
+                const bool last = sk_flag == nseg - 1;
+                __syncthreads();
+                if (!last) return;
+            }
+            // sum in k order, in place (device-scope loads: each slot was
+            // written once in this launch, by one workgroup, through to
+            // device scope before it was counted): a finisher that stored its partial
+            // reads it back (each lane reads what it wrote) and starts from
+            // segment 0's; one that did not is segment 0 and starts from its
+            // own accumulators
+            constexpr int GRP = CH < 8 ? CH : 8;  // chunks loaded at once (bounds the registers)
+            for (int jj = write ? 0 : 1; jj < nseg; ++jj) {
+                const float* src = slot(w0 + jj, x) + tid;
+#pragma unroll
+                for (int c0 = 0; c0 < CH; c0 += GRP) {
+                    f32x4 y[GRP];
+#pragma unroll
+                    for (int c = 0; c < GRP; ++c)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            y[c][e] = __hip_atomic_load(src + (4 * (c0 + c) + e) * NW * 64,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int c = 0; c < GRP; ++c)
+                        set_chunk(acc, c0 + c, jj == 0 ? y[c] : get_chunk(acc, c0 + c) + y[c]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            epilogue(em0, en0, 0);
+        };
+
+        // segments of this workgroup in order: the round tiles, then its
+        // stream-K range of the tail
+        int r = 0;
+        int64_t it = I > 0 ? it_of(v) : 0;
+        const int64_t it1 = I > 0 ? it_of(v + 1) : 0;
+        auto next_segment = [&](int& tile, int& ks, int& ke) __attribute__((always_inline)) {
+            if (r < R) {
+                tile = r++ * G + v;
+                ks = 0;
+                ke = S;
+                return true;
+            }
+            if (it >= it1) return false;
+            const int lt = (int)(it / S);
+            ks = (int)(it - (int64_t)lt * S);
+            ke = (int)min((int64_t)S, ks + (it1 - it));
+            tile = TB + lt;
+            it += ke - ks;
+            return true;
+        };
+        auto begin = [&](int tile, int ks) __attribute__((always_inline)) {
+            int tm, tn;
+            grouped_tile(tile, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+            start_tile(tm * BM, tn * BN, ks * BK);
+        };
+        int tile = 0, ks = 0, ke = 0;
+        bool have = next_segment(tile, ks, ke);
+        if (have) begin(tile, ks);
+        int par = 0;
+        bool pre = false;
+        while (have) {
+            zero_acc();
+            mainloop(ke - ks, par, pre);
+            const int em0 = m0, en0 = n0, ctile = tile, cks = ks, cke = ke;
+            have = next_segment(tile, ks, ke);
+            pre = false;
+            if (have) {
+                begin(tile, ks);
+                if constexpr (SK_PREFETCH) {
+                    // the next segment's first stage, into buffer 1
+                    issue_part(1, 0, 0, NDMA);
+                    pre = true;
+                }
+            }
+            finish(ctile, cks, cke, em0, en0);
+            par = pre ? 1 : 0;
+        }
+    }
 }
 
 }  // namespace dge

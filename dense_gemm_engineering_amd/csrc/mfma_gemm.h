@@ -93,6 +93,13 @@ struct MfmaArgs {
     int c_type;
     int vec_ok;  // 1 when A, B, C (and the loads' 16-byte chunks) are 16-byte aligned
     Epilogue ep;
+    // persistent stream-K schedule (direct-to-LDS kernel): stages per tile,
+    // partial-tile slots (2 x grid x BM x BN fp32) and per-tile arrival
+    // counters (zero at launch)
+    int sk_stages;
+    int sk_rounds;  // rounds of whole tiles before the stream-K tail
+    float* sk_ws;
+    unsigned* sk_cnt;
 };
 
 // Pack KPL elements loaded one by one (with a bound) into a 16-byte chunk.
@@ -277,7 +284,7 @@ __device__ inline void load_row8(const void* C, int64_t ldc, int row, int col, i
 // Epilogue for 8 consecutive columns of one row: alpha/beta/bias/GELU, one
 // rounding to the output type, store.
 template <int DT, int OT>
-__device__ inline void finish_row8(const MfmaArgs& p, int row, int col, const float* acc) {
+__device__ __attribute__((always_inline)) inline void finish_row8(const MfmaArgs& p, int row, int col, const float* acc) {
     const bool vec = p.vec_ok != 0;
     float old[8];
     if (p.ep.beta != 0.0f) load_row8<OT>(p.C, p.ldc, row, col, p.N, old, vec);
@@ -297,7 +304,7 @@ __device__ inline void finish_row8(const MfmaArgs& p, int row, int col, const fl
 // (SM rows x WTN columns, row pitch PITCH floats) whose first element is
 // C[grow0][gcol0].
 template <int DT, int MODE, int WTN, int SM, int PITCH>
-__device__ inline void drain_strip(const MfmaArgs& p, const float* stg, int grow0, int gcol0,
+__device__ __attribute__((always_inline)) inline void drain_strip(const MfmaArgs& p, const float* stg, int grow0, int gcol0,
                                    int split, int lane) {
     constexpr int LPR = WTN / 8;   // lanes per row, 8 columns each
     constexpr int RPP = 64 / LPR;  // rows per pass
@@ -343,7 +350,7 @@ __device__ inline void drain_strip(const MfmaArgs& p, const float* stg, int grow
 // Epilogue of a tile held as 16x16 accumulator blocks (16-row strips,
 // stg: NW x 16 x (WTN + 4) fp32).
 template <int DT, int BM, int BN, int WM, int WN, int MODE, int TM, int TN>
-__device__ inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], float* stg_all,
+__device__ __attribute__((always_inline)) inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], float* stg_all,
                                      int m0, int n0, int split) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile");
@@ -369,7 +376,7 @@ __device__ inline void epilogue_tile(const MfmaArgs& p, f32x4 (&acc)[TM][TN], fl
 // strips, stg: NW x 32 x (WTN + 8) fp32 (the pad puts the two row halves a
 // lane group writes in different banks).
 template <int DT, int BM, int BN, int WM, int WN, int MODE, int TM, int TN>
-__device__ inline void epilogue_tile32(const MfmaArgs& p, f32x16 (&acc)[TM][TN], float* stg_all,
+__device__ __attribute__((always_inline)) inline void epilogue_tile32(const MfmaArgs& p, f32x16 (&acc)[TM][TN], float* stg_all,
                                        int m0, int n0, int split) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile");

@@ -52,11 +52,13 @@
  *     overflow gives +-inf; subnormals are kept.
  *   - Unaligned pointers or leading dimensions that are not a multiple of
  *     16 bytes take a slower element-wise load path; they are not errors.
- *   - workspace: caller-owned device scratch for split-K partial sums.  If
- *     it is NULL or smaller than gemm_workspace_size(), the call runs
- *     without splitting K (it does not fail).
- *   - Split-K partial sums are reduced in fixed order (split 0, 1, ...), so
- *     results are bitwise reproducible run to run.
+ *   - workspace: caller-owned device scratch for split-K and stream-K
+ *     partial sums (and the stream-K arrival counters, which each call
+ *     clears itself).  If it is NULL or smaller than gemm_workspace_size(),
+ *     the call runs a schedule that fits (at worst without splitting K; it
+ *     does not fail).  Calls that share a workspace must not overlap.
+ *   - Split-K and stream-K partial sums are reduced in fixed order (K slice
+ *     0, 1, ...), so results are bitwise reproducible run to run.
  *   - Thread safety: calls may be issued concurrently from several host
  *     threads (distinct streams or not); the only shared state is a
  *     once-initialised device-property cache.
@@ -115,7 +117,7 @@ typedef enum {
                                  256, N <= 256, A 16-byte aligned with lda % 8 == 0);
                                  other problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO uses
                                  it for M >= 4096 and M >= 8N when eligible. */
-    GEMM_ALGO_DECODE = 6      /* decode shape: 1 <= M <= 64 input rows against an N x K
+    GEMM_ALGO_DECODE = 6,     /* decode shape: 1 <= M <= 64 input rows against an N x K
                                  weight (trans_b = 1, fp16/bf16, K % 8 == 0, A and B
                                  16-byte aligned with lda, ldb % 8 == 0), W streamed
                                  from memory straight into the MFMA operands, K split
@@ -124,6 +126,23 @@ typedef enum {
                                  whenever eligible ("Matrix Multiplication: The
                                  Operation Behind Modern AI", "The shape a language
                                  model actually runs"). */
+    GEMM_ALGO_STREAMK = 7     /* persistent stream-K schedule of the direct-to-LDS
+                                 kernels ("Optimizing GEMMs using tcgen05 - Part 2",
+                                 §8: stream-K for the tail and a persistent kernel
+                                 whose next tile's loads overlap this tile's
+                                 epilogue): one workgroup per CU slot, each taking an
+                                 equal contiguous share of the (tile, K stage)
+                                 iterations; partial tiles are summed in K order by
+                                 the segment that completes them.  Needs fp16/bf16,
+                                 full tiles, K % 64 == 0, aligned operands and
+                                 gemm_workspace_size_streamk() bytes of 16-byte
+                                 aligned workspace (GEMM_ERR_WORKSPACE with less);
+                                 other problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO
+                                 does not choose it: on MI355X it measured no faster
+                                 than the data-parallel and split-K schedules on
+                                 the square and prefill shapes (an XCD's workgroups
+                                 at different K stages share less of its L2, and
+                                 split tiles move fp32 partials through memory). */
 } gemm_algo_t;
 
 /* Tile configurations of the MFMA family (macro tile BM x BN, waves). */
@@ -264,6 +283,12 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype);
 
 /* Workspace bytes an explicit split into `splits` slices needs. */
 size_t gemm_workspace_size_splits(int64_t M, int64_t N, int splits);
+
+/* Workspace bytes the stream-K schedule (GEMM_ALGO_STREAMK) needs for this
+ * shape and tile (a gemm_tile_t; GEMM_TILE_AUTO = the largest over tiles) on
+ * the current device: two fp32 partial tiles per workgroup of the persistent
+ * grid, then one 32-bit arrival counter per tile.  0 for an empty problem. */
+size_t gemm_workspace_size_streamk(int64_t M, int64_t N, int64_t K, int tile);
 
 /* Static, NUL-terminated description of a status code. */
 const char* gemm_status_string(gemm_status_t s);
