@@ -312,6 +312,48 @@ size_t ws_bytes_for(int64_t M, int64_t N, int splits) {
     return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+// Column split: the first n1 columns as whole rounds of tile `tile` (every
+// CU slot busy for the full K), the other N - n1 columns as a problem of
+// their own with their best schedule (tile2, splits2).  It pays where the
+// plain schedule's last round is mostly empty but costs a full K: 2048 x
+// 11008 x 4096 has 344 tiles of 256 x 256 for 256 CUs, 1.34 rounds; as
+// 8192 columns (one round) + 2816 columns (smaller tiles, one short round)
+// it saves the empty part of the second round.  allowed2(n) gives the tiles
+// the rest may use.  Chosen only when the model says 3% or more.
+struct ColumnSplit {
+    int64_t n1;
+    int tile, tile2, splits2;
+};
+template <typename AllowedFn>
+bool choose_column_split(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws_bytes,
+                         unsigned allowed, AllowedFn allowed2, ColumnSplit* cs) {
+    const int bk = stage_k(dt);
+    int t0 = GEMM_TILE_AUTO, s0 = 0;
+    choose_schedule(M, N, K, dt, cus, ws_bytes, &t0, &s0, allowed);
+    double best = schedule_us(M, N, K, t0, s0, bk, cus) * 0.97;
+    bool found = false;
+    for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
+        if (!(allowed >> t & 1u)) continue;
+        const TileShape ts = tile_shape(t);
+        const int64_t tm = ceil_div(M, ts.bm), slots = (int64_t)cus * tile_occupancy(t);
+        if (M % ts.bm != 0 || slots % tm != 0) continue;
+        const int64_t cols = slots / tm;  // tile columns of one full round
+        const int64_t n1 = (N / ts.bn) / cols * cols * ts.bn;
+        if (n1 <= 0 || n1 >= N) continue;
+        const unsigned a2 = allowed2(N - n1);
+        if (!a2) continue;
+        int t2 = GEMM_TILE_AUTO, s2 = 0;
+        choose_schedule(M, N - n1, K, dt, cus, ws_bytes, &t2, &s2, a2);
+        const double us = schedule_us(M, n1, K, t, 1, bk, cus) + schedule_us(M, N - n1, K, t2, s2, bk, cus);
+        if (us < best) {
+            best = us;
+            found = true;
+            *cs = ColumnSplit{n1, t, t2, s2};
+        }
+    }
+    return found;
+}
+
 gemm_status_t launch_status(hipError_t e) {
     if (e == hipSuccess) return GEMM_OK;
     return GEMM_ERR_LAUNCH;
@@ -337,11 +379,50 @@ unsigned streamk_tiles(const Gemm& g) {
     return m;
 }
 
-// streamk: 1 = the stream-K schedule was asked for (it runs where eligible)
+// The fused q4 kernel's tiles: full tiles of an M x N problem.
+unsigned q4_tiles(int64_t M, int64_t N) {
+    unsigned m = 0;
+    for (int t = TILE_256x256; t <= TILE_LAST; ++t) {
+        const TileShape s = tile_shape(t);
+        if (M % s.bm == 0 && N % s.bn == 0) m |= 1u << t;
+    }
+    return m;
+}
+
+// Columns [c0, c0 + n) of g as a problem of its own (same A; B, C and the
+// bias offset to column c0).
+Gemm column_range(const Gemm& g, int64_t c0, int64_t n) {
+    Gemm h = g;
+    h.N = n;
+    if (g.b_q4)
+        h.B = (const char*)g.B + c0 * (g.K / 32) * 18;
+    else
+        h.B = (const char*)g.B + (g.trans_b ? c0 * g.ldb : c0) * in_bytes(g.dt);
+    h.C = (char*)g.C + c0 * out_bytes(g.c_type);
+    if (g.bias) h.bias = (const char*)g.bias + c0 * in_bytes(g.dt);
+    return h;
+}
+
+// streamk: 1 = the stream-K schedule was asked for (it runs where eligible);
+// colsplit: the automatic schedule may split the columns (not within a part)
 gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
-                       int streamk = 0) {
+                       int streamk = 0, bool colsplit = true) {
     if (tile != GEMM_TILE_AUTO && (tile < TILE_256x256 || tile > TILE_LAST))
         return GEMM_ERR_INVALID_VALUE;
+    if (colsplit && tile == GEMM_TILE_AUTO && splits == 0 && !streamk && direct &&
+        g.dt != IN_F32 && env_int("GEMM_COLSPLIT", 1) != 0) {
+        const unsigned all = g.b_q4 ? q4_tiles(g.M, g.N) : ~0u;
+        auto allowed2 = [&](int64_t n2) { return g.b_q4 ? q4_tiles(g.M, n2) : ~0u; };
+        ColumnSplit cs;
+        if (all && choose_column_split(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, all,
+                                       allowed2, &cs)) {
+            gemm_status_t st = run_mfma(column_range(g, 0, cs.n1), cs.tile, 1, cus, direct, 0, false);
+            if (st != GEMM_OK) return st;
+            // the rest with its tile; its split is chosen again against the
+            // workspace (the same choice, unless the workspace is misaligned)
+            return run_mfma(column_range(g, cs.n1, g.N - cs.n1), cs.tile2, 0, cus, direct, 0, false);
+        }
+    }
     const bool explicit_split = splits > 1;
     unsigned allowed = ~0u;
     if (g.b_q4) {
@@ -770,6 +851,12 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || dtype < IN_F16 || dtype > IN_F32) return 0;
     DeviceInfo dev{1, 256};
     if (current_device(&dev) != GEMM_OK) dev.cus = 256;
+    if (dtype != IN_F32) {
+        ColumnSplit cs;
+        if (choose_column_split(M, N, K, dtype, dev.cus, (size_t)-1, ~0u,
+                                [](int64_t) { return ~0u; }, &cs))
+            return ws_bytes_for(M, N - cs.n1, cs.splits2);
+    }
     int tile = GEMM_TILE_AUTO, s = 0;
     choose_schedule(M, N, K, dtype, dev.cus, (size_t)-1, &tile, &s);
     return ws_bytes_for(M, N, s);

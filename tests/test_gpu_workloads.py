@@ -139,3 +139,28 @@ def test_tall_skinny_bias_gelu_sampled_rows(N):
     b = oracle.decode(bias, "f16")
     T, U = oracle.gemm(X[rows], W, "f16", epi="bias_gelu", bias=b)
     assert_close(C[torch.from_numpy(rows).cuda()], T, U, bias=b, what="N=%d" % N)
+
+
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_column_split_schedule_integer_exact(trans_b, monkeypatch):
+    # 2048 x 11008: 344 tiles of 256 x 256 for 256 CUs, so the automatic
+    # schedule runs 8192 columns as one full round and the other 2816 on
+    # their own; small-integer inputs make every partial sum exact, so both
+    # parts (and the same problem without the column split) give the
+    # oracle's bits, bias included
+    M, N, K = 2048, 11008, 512
+    r = np.random.Generator(np.random.PCG64(9100 + trans_b))
+    A = inputs.to_bits(r.integers(-4, 5, (M, K)).astype(float), "f16")
+    B = inputs.to_bits(r.integers(-4, 5, (N, K) if trans_b else (K, N)).astype(float), "f16")
+    bias_bits = inputs.to_bits(r.integers(-8, 9, N).astype(float), "f16")
+    bias = oracle.decode(bias_bits, "f16")
+    T, _ = oracle.gemm(A, B, "f16", trans_b=trans_b, epi="bias", bias=bias, want_U=False)
+    n = dge.gemm_workspace_size(M, N, K, torch.float16)
+    ws = torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda")
+    for colsplit in ("1", "0"):
+        monkeypatch.setenv("GEMM_COLSPLIT", colsplit)
+        C = dge.gemm_f16(to_dev(A, "f16"), to_dev(B, "f16"), trans_b=trans_b,
+                         out_dtype=torch.float32, epi="bias", bias=to_dev(bias_bits, "f16"),
+                         workspace=ws)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what="colsplit=%s" % colsplit)
