@@ -9,10 +9,10 @@
 //    padded by 16 bytes) so that it can serve as the MFMA "A" operand of
 //    C^T = W^T X^T; the bias is staged next to it as fp32.  A wave reads all
 //    the W^T fragments of a 32-deep k-block at once (so their LDS latencies
-//    overlap) and, up to N = 160, applies each to two 16-row blocks.
+//    overlap) and, up to N = 64, applies each to two 16-row blocks.
 //  * X needs no LDS: the MFMA "B" operand of X^T is 8 consecutive k of one
 //    row of X per lane, i.e. a 16-byte load straight from memory into the
-//    operand registers.  Each wave owns 32 rows (16 for N > 160) at a time
+//    operand registers.  Each wave owns 16 rows (32 for N <= 64) at a time
 //    and issues their loads (K / 32 per lane and row block) before its first
 //    MFMA, and the next rows' loads before its epilogue.  The prologue asks
 //    for W and the bias before X and publishes W with an LDS-only barrier,
@@ -42,13 +42,14 @@ struct SkinnyArgs {
 };
 
 constexpr int SKINNY_KBMAX = 8;        // K <= 256
-// 16-row blocks per wave: two while the accumulators leave room (N <= 160),
-// else one.
-__host__ __device__ constexpr int skinny_rb(int nt) { return nt <= 10 ? 2 : 1; }
-// k-blocks of X (32 k each) held in registers at a time: all of K <= 256,
-// or 5 (K <= 160 in one round trip) for N = 160 with two row blocks.  A K
-// with more k-blocks than this takes a second round trip per step.
-__host__ __device__ constexpr int skinny_kch(int nt) { return nt >= 8 && nt <= 10 ? 5 : 8; }
+// 16-row blocks per wave and step: two for N <= 64, else one.  For N = 160
+// one block per step gives each wave two steps at 65536 rows, so one step's
+// stores overlap the next step's loads (measured 19.7 -> 18.3 us HBM-cold);
+// for N = 32 the two ways measure the same.
+__host__ __device__ constexpr int skinny_rb(int nt) { return nt <= 4 ? 2 : 1; }
+// k-blocks of X (32 k each) held in registers at a time: all of K <= 256
+// (with one row block per step the registers allow it for every N).
+__host__ __device__ constexpr int skinny_kch(int) { return 8; }
 // Waves per workgroup at most (256 registers per lane).
 __host__ __device__ constexpr int skinny_max_waves(int) { return 8; }
 
