@@ -339,6 +339,18 @@ def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
     return out
 
 
+def bench_bf16_square(dge, inputs, torch, steps):
+    """The 4096^3 workload with bf16 operands (N(0,1)/sqrt(K)), fp16 output."""
+    A, B = inputs.square4096("bf16")
+    dA, dB = _dev(A, "bf16", torch), _dev(B, "bf16", torch)
+    C = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
+    n = dge.gemm_workspace_size(4096, 4096, 4096, torch.bfloat16)
+    ws = torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda") if n else None
+    t, _ = time_launches(lambda: dge.gemm_bf16(dA, dB, C, workspace=ws), steps, 3, torch)
+    tf = gemm_flops(4096, 4096, 4096) / t / 1e12
+    return {"us": t * 1e6, "TFLOPs": tf, "mfma_frac": tf / PEAK["bf16"]}
+
+
 def bench_ladder(dge, inputs, torch, steps):
     out = {}
     for n in (1024, 2048, 4096):
@@ -449,6 +461,8 @@ def main():
         line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps)
         line["prefill_kquant"] = bench_kquant(dge, inputs, torch, extra_steps,
                                               line["prefill_2048"])
+        if args.dtype == "f16":
+            line["bf16_4096"] = bench_bf16_square(dge, inputs, torch, extra_steps)
         line["streamk_vs_default"] = bench_streamk(dge, inputs, torch, extra_steps)
         line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps)
         line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps)
