@@ -348,15 +348,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         else
             read_bt(lb, kb, b);
     };
-    // MFMAs [lo, hi) of one k-block, row-major over the TM x TN blocks.
+    // MFMAs [lo, hi) of one k-block over the TM x TN blocks in serpentine
+    // order (row i left to right, row i + 1 right to left), so consecutive
+    // MFMAs share an operand fragment also where the rows change: fewer input
+    // bits toggle in the matrix unit, which is power-bound here (measured
+    // ~1.6% faster with an N x K B, no change with K x N).
     auto mma_range = [&](const u32x4* a, const u32x4* b, int lo, int hi) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < TM * TN; ++x)
             if (x >= lo && x < hi) {
+                const int i = x / TN, j = (i & 1) ? TN - 1 - x % TN : x % TN;
                 if constexpr (MS == 32)
-                    mma32<DT>(acc[x / TN][x % TN], a[x / TN], b[x % TN]);
+                    mma32<DT>(acc[i][j], a[i], b[j]);
                 else
-                    mma_chunk<DT>(acc[x / TN][x % TN], a[x / TN], b[x % TN]);
+                    mma_chunk<DT>(acc[i][j], a[i], b[j]);
             }
     };
 
