@@ -361,11 +361,19 @@ gemm_status_t launch_status(hipError_t e) {
 
 // direct: 0 = register-staged kernel only, 1 = direct-to-LDS kernel when the
 // problem qualifies (full tiles, 16-bit inputs, aligned operands).
+// The direct-to-LDS kernels address each load as a wave-uniform base plus a
+// 32-bit per-lane byte offset of up to 32 rows: leading dimensions below 2^24
+// elements keep it under 2^31.
+bool direct_ld_ok(const Gemm& g) {
+    return g.lda < ((int64_t)1 << 24) && (g.b_q4 || g.ldb < ((int64_t)1 << 24));
+}
+
 // Tiles whose stream-K schedule can run this problem: the direct-to-LDS
 // kernel's conditions (16-bit inputs, full tiles, whole stages, aligned
 // operands, and for a K x N B at least 128 columns).
 unsigned streamk_tiles(const Gemm& g) {
-    if (g.b_q4 || g.dt == IN_F32 || g.K <= 0 || g.K % stage_k(g.dt) != 0) return 0;
+    if (g.b_q4 || g.dt == IN_F32 || g.K <= 0 || g.K % stage_k(g.dt) != 0 || !direct_ld_ok(g))
+        return 0;
     if (env_int("GEMM_DIRECT", 1) == 0 || env_int("GEMM_STREAMK", 1) == 0) return 0;
     const int vec_el = 16 / in_bytes(g.dt);
     const bool vec = aligned16(g.A) && aligned16(g.B) && aligned16(g.C) && g.lda % vec_el == 0 &&
@@ -434,7 +442,7 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
             if (g.M % s.bm == 0 && g.N % s.bn == 0) allowed |= 1u << t;
         }
         if (tile != GEMM_TILE_AUTO) allowed &= 1u << tile;
-        const bool ok = allowed && g.K % 64 == 0 && ((uintptr_t)g.B & 3) == 0 && aligned16(g.A) &&
+        const bool ok = allowed && g.K % 64 == 0 && direct_ld_ok(g) && ((uintptr_t)g.B & 3) == 0 && aligned16(g.A) &&
                         aligned16(g.C) && g.lda % 8 == 0 && (g.ldc * out_bytes(g.c_type)) % 16 == 0;
         if (!ok) return GEMM_ERR_NOT_SUPPORTED;
     }
@@ -504,7 +512,7 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
             e = launch_splitk_fixup(g.dt, simple_args(g), (const float*)g.ws, splits, g.stream);
         return launch_status(e);
     }
-    const bool use_direct = direct && fast && g.dt != IN_F32 &&
+    const bool use_direct = direct && fast && g.dt != IN_F32 && direct_ld_ok(g) &&
                             (g.trans_b || ts.bn >= 128) && env_int("GEMM_DIRECT", 1) != 0;
     if (sk && use_direct && aligned16(g.ws)) {
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n, S = g.K / bk;

@@ -95,6 +95,15 @@ __device__ inline void lds_dma16(const void* g, DGE_LDS void* l) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(la)
                  : "memory", "m0");
 }
+// The same with the address split into a wave-uniform 64-bit base (scalar
+// registers) and a 32-bit per-lane byte offset: a stage's advance is then
+// scalar arithmetic on the base, and the per-lane offsets stay constant.
+__device__ inline void lds_dma16_s(const void* sbase, uint32_t voff, DGE_LDS void* l) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(la)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ inline uint2 ds_read_tr(const DGE_LDS char* p) {
@@ -191,7 +200,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     __shared__ int sk_flag;  // stream-K: a counter value broadcast to the workgroup
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: in a scalar register, the per-wave LDS
+    // bases of the direct loads need no per-stage readfirstlane
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
 
     // ---- per-lane global source offsets (elements) for the direct loads
@@ -199,26 +210,43 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // its chunk swizzle depends on the row block, so it is applied per instruction
     const int a_row = 8 * wave * IA + (lane >> 3);
     const int k_lane_chunk = lane & 7;
-    const int64_t a_step = (int64_t)8 * p.lda;  // next instruction: 8 rows down
     // B (K x N): instruction i fills k-rows RPI * (wave * IB + i) + lane / CPR;
     // the chunk swizzle depends on the k-row, so it is applied per instruction
-    const int64_t b_step = TRANS_B ? (int64_t)8 * p.ldb : (int64_t)RPI_B * p.ldb;
-    // the current tile: origin (m0, n0), first k kbeg, and the sources there
+    const int b_lane_chunk = lane % CPR_B;
+    const int b_krow0 = RPI_B * wave * IB + lane / CPR_B;
+    // per-lane byte offsets of each direct load from the wave's base (row or
+    // k-row within the wave's block, swizzled chunk); constant for the kernel
+    // (the host keeps them below 2^31: leading dimensions under 2^24)
+    uint32_t a_off[IA > 0 ? IA : 1], b_off[IB > 0 ? IB : 1];
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+        a_off[i] = (uint32_t)((((lane >> 3) + 8 * i) * p.lda +
+                               (k_lane_chunk ^ swz_k<MS>(a_row + 8 * i)) * 8) * 2);
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        if constexpr (TRANS_B)
+            b_off[i] = (uint32_t)((((lane >> 3) + 8 * i) * p.ldb +
+                                   (k_lane_chunk ^ swz_k<MS>(8 * wave * IB + (lane >> 3) + 8 * i)) * 8) * 2);
+        else
+            b_off[i] = (uint32_t)(((lane / CPR_B + RPI_B * i) * p.ldb +
+                                   (b_lane_chunk ^ swz_b<MS>(b_krow0 + RPI_B * i)) * 8) * 2);
+    }
+    // the current tile: origin (m0, n0), first k kbeg, and the wave-uniform
+    // bases of its direct loads (A: the wave's first row at kbeg; B: the
+    // wave's first row (N x K) or k-row (K x N))
     int m0 = 0, n0 = 0, kbeg = 0;
-    const uint16_t* a_src = nullptr;
-    const uint16_t* b_src = nullptr;
+    const char* a_base = nullptr;
+    const char* b_base = nullptr;
     auto start_tile = [&](int tm0, int tn0, int tk0) __attribute__((always_inline)) {
         m0 = tm0;
         n0 = tn0;
         kbeg = tk0;
-        a_src = (const uint16_t*)p.A + (int64_t)(m0 + a_row) * p.lda + kbeg;
+        a_base = (const char*)p.A + ((int64_t)(m0 + 8 * wave * IA) * p.lda + kbeg) * 2;
         if constexpr (TRANS_B)
-            b_src = (const uint16_t*)p.B + (int64_t)(n0 + 8 * wave * IB + (lane >> 3)) * p.ldb + kbeg;
+            b_base = (const char*)p.B + ((int64_t)(n0 + 8 * wave * IB) * p.ldb + kbeg) * 2;
         else
-            b_src = (const uint16_t*)p.B + (int64_t)(kbeg + RPI_B * wave * IB + lane / CPR_B) * p.ldb + n0;
+            b_base = (const char*)p.B + ((int64_t)(kbeg + RPI_B * wave * IB) * p.ldb + n0) * 2;
     };
-    const int b_lane_chunk = lane % CPR_B;
-    const int b_krow0 = RPI_B * wave * IB + lane / CPR_B;
     const int64_t a_kstep = BK;                                        // A per stage
     const int64_t b_kstep = TRANS_B ? (int64_t)BK : (int64_t)BK * p.ldb;  // B per stage
 
@@ -226,24 +254,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     auto issue_part = [&](int st, int kt, int lo, int hi) __attribute__((always_inline)) {
         DGE_LDS char* la = (DGE_LDS char*)&lds[st][0] + wave * IA * 1024;
         DGE_LDS char* lb = (DGE_LDS char*)&lds[st][A_BYTES] + wave * IB * 1024;
-        const uint16_t* ga = a_src + kt * a_kstep;
-        const uint16_t* gb = b_src + kt * b_kstep;
+        const char* ga = a_base + kt * a_kstep * 2;
+        const char* gb = b_base + kt * b_kstep * 2;
 #pragma unroll
         for (int i = 0; i < IA; ++i) {
             if (i < lo || i >= hi) continue;
-            const int chunk = k_lane_chunk ^ swz_k<MS>(a_row + 8 * i);
-            lds_dma16(ga + i * a_step + chunk * 8, la + i * 1024);
+            lds_dma16_s(ga, a_off[i], la + i * 1024);
         }
 #pragma unroll
         for (int i = 0; i < IB; ++i) {
             if (IA + i < lo || IA + i >= hi) continue;
-            if constexpr (TRANS_B) {
-                const int chunk = k_lane_chunk ^ swz_k<MS>(8 * wave * IB + (lane >> 3) + 8 * i);
-                lds_dma16(gb + i * b_step + chunk * 8, lb + i * 1024);
-            } else {
-                const int chunk = b_lane_chunk ^ swz_b<MS>(b_krow0 + RPI_B * i);
-                lds_dma16(gb + i * b_step + chunk * 8, lb + i * 1024);
-            }
+            lds_dma16_s(gb, b_off[i], lb + i * 1024);
         }
     };
 
