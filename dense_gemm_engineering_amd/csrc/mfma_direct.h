@@ -63,6 +63,7 @@
 namespace dge {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define DGE_LDS __attribute__((address_space(3)))
 
 template <int MS>
@@ -166,6 +167,114 @@ __device__ inline void q4_decode4(uint32_t nib, h2v d2, uint32_t* o) {
     o[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2v, v23) - off) * d2);
 }
 
+// Epilogue of a tile held as transposed 16x16 blocks (the MFMA operands
+// swapped, so the block is C^T): lane l holds, of block (i, j), row
+// 16 i + (l & 15) and the 4 consecutive columns 16 j + 4 (l / 16) + e.
+// alpha, beta (4 consecutive old values), bias, GELU and the rounding run in
+// registers; 16-bit results go through the wave's own 8 KB of LDS (4 blocks
+// of rows at a time, 16-byte chunks XOR-swizzled by row) and leave as
+// 16-byte row pieces, 8 lanes per 128-byte row: no workgroup barrier.  fp32
+// results and split-K partials leave straight from registers (16 bytes per
+// lane, 4 lanes per 64-byte row piece).  Full tiles, 16-byte aligned rows.
+template <int DT, int OT, int BM, int BN, int WM, int WN, int TM, int TN>
+__device__ __attribute__((always_inline)) inline void epilogue_tile_t16_ot(
+    const MfmaArgs& p, f32x4 (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0, int wm0, int wn0,
+    int lane) {
+    typedef typename OutType<OT>::T T;
+    const int rl = lane & 15, cl = 4 * (lane >> 4);
+    float bias[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            bias[j][e] = p.ep.epi != EPI_NONE ? load_elem<DT>(p.ep.bias, n0 + wn0 + 16 * j + cl + e) : 0.0f;
+    const bool gelu = p.ep.epi == EPI_BIAS_GELU, beta = p.ep.beta != 0.0f;
+    auto finish4 = [&](int i, int j, float* t) __attribute__((always_inline)) {
+        const int64_t row = m0 + wm0 + 16 * i + rl, col = n0 + wn0 + 16 * j + cl;
+        float old[4] = {0.f, 0.f, 0.f, 0.f};
+        if (beta) {
+            const T* c = (const T*)p.C + row * p.ldc + col;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) old[e] = OutType<OT>::to_f32(c[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = p.ep.alpha * acc[i][j][e];
+            if (beta) v += p.ep.beta * old[e];
+            v += bias[j][e];
+            t[e] = gelu ? gelu_tanh(v) : v;
+        }
+    };
+    if constexpr (OT == OUT_F32) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                float t[4];
+                finish4(i, j, t);
+                float* c = (float*)p.C + (int64_t)(m0 + wm0 + 16 * i + rl) * p.ldc + n0 + wn0 + 16 * j + cl;
+                *(f32x4*)c = (f32x4){t[0], t[1], t[2], t[3]};
+            }
+    } else {
+        static_assert(TN * 16 * 2 == 128, "a staged row is 128 bytes (64 columns)");
+        constexpr int IP = 4;  // row blocks per pass: 64 rows x 128 bytes = 8 KB
+#pragma unroll
+        for (int i0 = 0; i0 < TM; i0 += IP) {
+#pragma unroll
+            for (int i = i0; i < i0 + IP; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    float t[4];
+                    finish4(i, j, t);
+                    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[0])) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[1])) << 16);
+                    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[2])) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[3])) << 16);
+                    const int r = 16 * (i - i0) + rl, ch = 2 * j + (lane >> 5);
+                    *(DGE_LDS u32x2*)(stg + r * 128 + ((ch ^ (r & 7)) << 4) + 8 * ((lane >> 4) & 1)) =
+                        (u32x2){lo, hi};
+                }
+            // this wave's rows back as 16-byte pieces (the wave's own LDS
+            // operations complete in order: no barrier)
+#pragma unroll
+            for (int q = 0; q < IP * 16 / 8; ++q) {
+                const int r = 8 * q + (lane >> 3), ch = lane & 7;
+                const u32x4 v = *(const DGE_LDS u32x4*)(stg + r * 128 + ((ch ^ (r & 7)) << 4));
+                T* c = (T*)p.C + (int64_t)(m0 + wm0 + 16 * i0 + r) * p.ldc + n0 + wn0 + 8 * ch;
+                *(u32x4*)c = v;
+            }
+        }
+    }
+}
+
+template <int DT, int BM, int BN, int WM, int WN, int TM, int TN>
+__device__ __attribute__((always_inline)) inline void epilogue_tile_t16(
+    const MfmaArgs& p, f32x4 (&acc)[TM][TN], DGE_LDS char* stg_all, int m0, int n0, int split) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile");
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
+    if (p.ws) {  // split-K partial sums: fp32, no epilogue
+        const int rl = lane & 15, cl = 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t row = m0 + wm0 + 16 * i + rl;
+                float* w = p.ws + ((int64_t)split * p.M + row) * p.N + n0 + wn0 + 16 * j + cl;
+                *(f32x4*)w = acc[i][j];
+            }
+        return;
+    }
+    DGE_LDS char* stg = stg_all + wave * 8192;
+    if (p.c_type == OUT_F16)
+        epilogue_tile_t16_ot<DT, OUT_F16, BM, BN, WM, WN, TM, TN>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    else if (p.c_type == OUT_BF16)
+        epilogue_tile_t16_ot<DT, OUT_BF16, BM, BN, WM, WN, TM, TN>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    else
+        epilogue_tile_t16_ot<DT, OUT_F32, BM, BN, WM, WN, TM, TN>(p, acc, stg, m0, n0, wm0, wn0, lane);
+}
+
 template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS, bool Q4 = false,
           bool SK = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p) {
@@ -189,8 +298,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int CPR_B = BN / 8;             // 16-byte chunks per k-row of a K x N B tile
     constexpr int RPI_B = 1024 / (BN * 2);    // k-rows per 1 KB direct-load instruction
     static_assert(TRANS_B || RPI_B * BN * 2 == 1024, "whole k-rows per instruction");
-    // epilogue staging (from buffer 0 on): one MS-row strip per wave
-    constexpr int STG_BYTES = NW * MS * (WTN + (MS == 32 ? 8 : 4)) * 4;
+    // epilogue staging (from buffer 0 on): 8 KB per wave for transposed
+    // 16x16 blocks, one 32-row fp32 strip per wave for 32x32 blocks
+    constexpr int STG_BYTES = MS == 16 ? NW * 8192 : NW * 32 * (WTN + 8) * 4;
     static_assert(STG_BYTES <= 2 * (A_BYTES + B_BYTES), "epilogue staging fits");
     // stream-K: the next tile's first stage can load into buffer 1 during the
     // epilogue only where the staging stays inside buffer 0
@@ -381,8 +491,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
                 const int i = x / TN, j = (i & 1) ? TN - 1 - x % TN : x % TN;
                 if constexpr (MS == 32)
                     mma32<DT>(acc[i][j], a[i], b[j]);
-                else
-                    mma_chunk<DT>(acc[i][j], a[i], b[j]);
+                else  // operands swapped: the block is C^T (the epilogue's layout)
+                    mma_chunk<DT>(acc[i][j], b[j], a[i]);
             }
     };
 
@@ -476,7 +586,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         if constexpr (MS == 32)
             epilogue_tile32<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], em0, en0, split);
         else
-            epilogue_tile<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], em0, en0, split);
+            epilogue_tile_t16<DT, BM, BN, WM, WN>(p, acc, (DGE_LDS char*)&lds[0][0], em0, en0, split);
     };
 
     if constexpr (!SK) {
@@ -651,6 +761,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
                 }
             }
             finish(ctile, cks, cke, em0, en0);
+            // the epilogue stages through buffer 0 without a closing barrier;
+            // the next segment loads into it once every wave is done
+            __syncthreads();
             par = pre ? 1 : 0;
         }
     }
