@@ -167,30 +167,47 @@ __device__ inline void q4_decode4(uint32_t nib, h2v d2, uint32_t* o) {
     o[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2v, v23) - off) * d2);
 }
 
-// Epilogue of a tile held as transposed 16x16 blocks (the MFMA operands
-// swapped, so the block is C^T): lane l holds, of block (i, j), row
-// 16 i + (l & 15) and the 4 consecutive columns 16 j + 4 (l / 16) + e.
-// alpha, beta (4 consecutive old values), bias, GELU and the rounding run in
-// registers; 16-bit results go through the wave's own 8 KB of LDS (4 blocks
-// of rows at a time, 16-byte chunks XOR-swizzled by row) and leave as
-// 16-byte row pieces, 8 lanes per 128-byte row: no workgroup barrier.  fp32
-// results and split-K partials leave straight from registers (16 bytes per
-// lane, 4 lanes per 64-byte row piece).  Full tiles, 16-byte aligned rows.
-template <int DT, int OT, int BM, int BN, int WM, int WN, int TM, int TN>
-__device__ __attribute__((always_inline)) inline void epilogue_tile_t16_ot(
-    const MfmaArgs& p, f32x4 (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0, int wm0, int wn0,
-    int lane) {
+// Epilogue of a tile held as transposed MS x MS blocks (the MFMA operands
+// swapped, so each block is C^T): lane l holds, of block (i, j), row
+// MS i + (l % MS) and NG groups of 4 consecutive columns, group g at column
+// MS j + CG g + 4 (l / MS) (MS = 16: one group, CG unused; MS = 32: four
+// groups, CG = 8), accumulator elements 4 g .. 4 g + 3.  alpha, beta (4
+// consecutive old values), bias, GELU and the rounding run in registers;
+// 16-bit results go through the wave's own part of LDS (IP row blocks at a
+// time, 16-byte chunks XOR-swizzled by row) and leave as 16-byte row
+// pieces: no workgroup barrier.  fp32 results and split-K partials leave
+// straight from registers, 16 bytes per lane.  Full tiles, 16-byte aligned
+// rows.
+template <int MS> struct TLayout;
+template <> struct TLayout<16> { static constexpr int NG = 1, CG = 0; };
+template <> struct TLayout<32> { static constexpr int NG = 4, CG = 8; };
+
+template <int DT, int OT, int MS, int WTM, int WTN, int TM, int TN, int IP>
+__device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
+    const MfmaArgs& p, typename AccBlock<MS>::T (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0,
+    int wm0, int wn0, int lane) {
     typedef typename OutType<OT>::T T;
-    const int rl = lane & 15, cl = 4 * (lane >> 4);
-    float bias[TN][4];
+    constexpr int NG = TLayout<MS>::NG, CG = TLayout<MS>::CG;
+    const int rl = lane % MS, cl = 4 * (lane / MS);
+    // the lane's bias values: held in registers when few (16 for the 8-wave
+    // tile), else loaded per group of 4 columns (the 4-wave tiles keep 256
+    // accumulators live)
+    constexpr bool PRE_BIAS = TN * NG * 4 <= 16;
+    const bool has_bias = p.ep.epi != EPI_NONE;
+    float bias[PRE_BIAS ? TN : 1][PRE_BIAS ? NG : 1][4];
+    if constexpr (PRE_BIAS) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            bias[j][e] = p.ep.epi != EPI_NONE ? load_elem<DT>(p.ep.bias, n0 + wn0 + 16 * j + cl + e) : 0.0f;
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bias[j][g][e] =
+                        has_bias ? load_elem<DT>(p.ep.bias, n0 + wn0 + MS * j + CG * g + cl + e) : 0.0f;
+    }
     const bool gelu = p.ep.epi == EPI_BIAS_GELU, beta = p.ep.beta != 0.0f;
-    auto finish4 = [&](int i, int j, float* t) __attribute__((always_inline)) {
-        const int64_t row = m0 + wm0 + 16 * i + rl, col = n0 + wn0 + 16 * j + cl;
+    auto finish4 = [&](int i, int j, int g, float* t) __attribute__((always_inline)) {
+        const int64_t row = m0 + wm0 + MS * i + rl, col = n0 + wn0 + MS * j + CG * g + cl;
         float old[4] = {0.f, 0.f, 0.f, 0.f};
         if (beta) {
             const T* c = (const T*)p.C + row * p.ldc + col;
@@ -199,9 +216,12 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t16_ot(
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float v = p.ep.alpha * acc[i][j][e];
+            float v = p.ep.alpha * acc[i][j][4 * g + e];
             if (beta) v += p.ep.beta * old[e];
-            v += bias[j][e];
+            if constexpr (PRE_BIAS)
+                v += bias[j][g][e];
+            else if (has_bias)
+                v += load_elem<DT>(p.ep.bias, col + e);
             t[e] = gelu ? gelu_tanh(v) : v;
         }
     };
@@ -209,70 +229,88 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t16_ot(
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                float t[4];
-                finish4(i, j, t);
-                float* c = (float*)p.C + (int64_t)(m0 + wm0 + 16 * i + rl) * p.ldc + n0 + wn0 + 16 * j + cl;
-                *(f32x4*)c = (f32x4){t[0], t[1], t[2], t[3]};
-            }
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    float t[4];
+                    finish4(i, j, g, t);
+                    float* c = (float*)p.C + (int64_t)(m0 + wm0 + MS * i + rl) * p.ldc + n0 + wn0 +
+                               MS * j + CG * g + cl;
+                    *(f32x4*)c = (f32x4){t[0], t[1], t[2], t[3]};
+                }
     } else {
-        static_assert(TN * 16 * 2 == 128, "a staged row is 128 bytes (64 columns)");
-        constexpr int IP = 4;  // row blocks per pass: 64 rows x 128 bytes = 8 KB
+        constexpr int RB = WTN * 2;    // bytes of a staged row
+        constexpr int CPR = RB / 16;   // 16-byte chunks per row (a power of two)
+        static_assert((CPR & (CPR - 1)) == 0 && CPR >= 4 && TM % IP == 0, "staging layout");
 #pragma unroll
         for (int i0 = 0; i0 < TM; i0 += IP) {
 #pragma unroll
             for (int i = i0; i < i0 + IP; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    float t[4];
-                    finish4(i, j, t);
-                    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[0])) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[1])) << 16);
-                    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[2])) |
-                                        ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[3])) << 16);
-                    const int r = 16 * (i - i0) + rl, ch = 2 * j + (lane >> 5);
-                    *(DGE_LDS u32x2*)(stg + r * 128 + ((ch ^ (r & 7)) << 4) + 8 * ((lane >> 4) & 1)) =
-                        (u32x2){lo, hi};
-                }
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        float t[4];
+                        finish4(i, j, g, t);
+                        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[0])) |
+                                            ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[1])) << 16);
+                        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[2])) |
+                                            ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[3])) << 16);
+                        const int r = MS * (i - i0) + rl;
+                        const int cb = (MS * j + CG * g + cl) * 2;  // byte column in the row
+                        *(DGE_LDS u32x2*)(stg + r * RB + (((cb >> 4) ^ (r & (CPR - 1))) << 4) + (cb & 15)) =
+                            (u32x2){lo, hi};
+                    }
             // this wave's rows back as 16-byte pieces (the wave's own LDS
             // operations complete in order: no barrier)
 #pragma unroll
-            for (int q = 0; q < IP * 16 / 8; ++q) {
-                const int r = 8 * q + (lane >> 3), ch = lane & 7;
-                const u32x4 v = *(const DGE_LDS u32x4*)(stg + r * 128 + ((ch ^ (r & 7)) << 4));
-                T* c = (T*)p.C + (int64_t)(m0 + wm0 + 16 * i0 + r) * p.ldc + n0 + wn0 + 8 * ch;
+            for (int q = 0; q < IP * MS * CPR / 64; ++q) {
+                const int r = q * (64 / CPR) + lane / CPR, ch = lane % CPR;
+                const u32x4 v = *(const DGE_LDS u32x4*)(stg + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
+                T* c = (T*)p.C + (int64_t)(m0 + wm0 + MS * i0 + r) * p.ldc + n0 + wn0 + 8 * ch;
                 *(u32x4*)c = v;
             }
         }
     }
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int TM, int TN>
-__device__ __attribute__((always_inline)) inline void epilogue_tile_t16(
-    const MfmaArgs& p, f32x4 (&acc)[TM][TN], DGE_LDS char* stg_all, int m0, int n0, int split) {
+// STG: LDS bytes the staging may use (it starts at stg_all); each wave gets
+// STG / waves, and as many row blocks per pass as fit.
+template <int DT, int BM, int BN, int WM, int WN, int MS, int TM, int TN, int STG>
+__device__ __attribute__((always_inline)) inline void epilogue_tile_t(
+    const MfmaArgs& p, typename AccBlock<MS>::T (&acc)[TM][TN], DGE_LDS char* stg_all, int m0,
+    int n0, int split) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    static_assert(TM * 16 == WTM && TN * 16 == WTN, "wave tile");
+    static_assert(TM * MS == WTM && TN * MS == WTN, "wave tile");
+    constexpr int NG = TLayout<MS>::NG, CG = TLayout<MS>::CG;
+    constexpr int PER_WAVE = STG / (WM * WN);
+    constexpr int IP0 = PER_WAVE / (MS * WTN * 2);
+    constexpr int IP = IP0 >= TM ? TM : (IP0 >= 4 ? 4 : (IP0 >= 2 ? 2 : 1));
+    static_assert(IP0 >= 1, "a row block of the wave tile fits the staging");
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
     if (p.ws) {  // split-K partial sums: fp32, no epilogue
-        const int rl = lane & 15, cl = 4 * (lane >> 4);
+        const int rl = lane % MS, cl = 4 * (lane / MS);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t row = m0 + wm0 + 16 * i + rl;
-                float* w = p.ws + ((int64_t)split * p.M + row) * p.N + n0 + wn0 + 16 * j + cl;
-                *(f32x4*)w = acc[i][j];
-            }
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int64_t row = m0 + wm0 + MS * i + rl;
+                    float* w = p.ws + ((int64_t)split * p.M + row) * p.N + n0 + wn0 + MS * j + CG * g + cl;
+                    *(f32x4*)w = (f32x4){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                         acc[i][j][4 * g + 3]};
+                }
         return;
     }
-    DGE_LDS char* stg = stg_all + wave * 8192;
+    DGE_LDS char* stg = stg_all + wave * PER_WAVE;
     if (p.c_type == OUT_F16)
-        epilogue_tile_t16_ot<DT, OUT_F16, BM, BN, WM, WN, TM, TN>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_ot<DT, OUT_F16, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
     else if (p.c_type == OUT_BF16)
-        epilogue_tile_t16_ot<DT, OUT_BF16, BM, BN, WM, WN, TM, TN>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_ot<DT, OUT_BF16, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
     else
-        epilogue_tile_t16_ot<DT, OUT_F32, BM, BN, WM, WN, TM, TN>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_ot<DT, OUT_F32, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
 }
 
 template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS, bool Q4 = false,
@@ -298,13 +336,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int CPR_B = BN / 8;             // 16-byte chunks per k-row of a K x N B tile
     constexpr int RPI_B = 1024 / (BN * 2);    // k-rows per 1 KB direct-load instruction
     static_assert(TRANS_B || RPI_B * BN * 2 == 1024, "whole k-rows per instruction");
-    // epilogue staging (from buffer 0 on): 8 KB per wave for transposed
-    // 16x16 blocks, one 32-row fp32 strip per wave for 32x32 blocks
-    constexpr int STG_BYTES = MS == 16 ? NW * 8192 : NW * 32 * (WTN + 8) * 4;
-    static_assert(STG_BYTES <= 2 * (A_BYTES + B_BYTES), "epilogue staging fits");
-    // stream-K: the next tile's first stage can load into buffer 1 during the
-    // epilogue only where the staging stays inside buffer 0
-    constexpr bool SK_PREFETCH = STG_BYTES <= A_BYTES + B_BYTES;
 
     __shared__ __attribute__((aligned(1024))) char lds[2][A_BYTES + B_BYTES];
     __shared__ int sk_flag;  // stream-K: a counter value broadcast to the workgroup
@@ -489,9 +520,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         for (int x = 0; x < TM * TN; ++x)
             if (x >= lo && x < hi) {
                 const int i = x / TN, j = (i & 1) ? TN - 1 - x % TN : x % TN;
+                // operands swapped: the block is C^T (the epilogue's layout)
                 if constexpr (MS == 32)
-                    mma32<DT>(acc[i][j], a[i], b[j]);
-                else  // operands swapped: the block is C^T (the epilogue's layout)
+                    mma32<DT>(acc[i][j], b[j], a[i]);
+                else
                     mma_chunk<DT>(acc[i][j], b[j], a[i]);
             }
     };
@@ -583,10 +615,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
 
     // the fused epilogue of tile (em0, en0), staged through buffer 0
     auto epilogue = [&](int em0, int en0, int split) __attribute__((always_inline)) {
-        if constexpr (MS == 32)
-            epilogue_tile32<DT, BM, BN, WM, WN, LOAD_FAST>(p, acc, (float*)&lds[0][0], em0, en0, split);
-        else
-            epilogue_tile_t16<DT, BM, BN, WM, WN>(p, acc, (DGE_LDS char*)&lds[0][0], em0, en0, split);
+        epilogue_tile_t<DT, BM, BN, WM, WN, MS, TM, TN, A_BYTES + B_BYTES>(
+            p, acc, (DGE_LDS char*)&lds[0][0], em0, en0, split);
     };
 
     if constexpr (!SK) {
@@ -615,9 +645,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         // segments of the tile in k order (bitwise the same sum whichever
         // segment finishes) and runs the epilogue.  No workgroup ever waits
         // for another.  Between segments, the next tile's first stage is
-        // loaded into buffer 1 while the epilogue stages through buffer 0
-        // (tiles whose staging fits in buffer 0: 256 x 256 with 8 waves,
-        // 256 x 128 and 128 x 64).
+        // loaded into buffer 1 while the epilogue stages through buffer 0.
         const int G = gridDim.x;
         const int v = remap_xcd(blockIdx.x, G);
         const int S = p.sk_stages;
@@ -754,11 +782,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             pre = false;
             if (have) {
                 begin(tile, ks);
-                if constexpr (SK_PREFETCH) {
-                    // the next segment's first stage, into buffer 1
-                    issue_part(1, 0, 0, NDMA);
-                    pre = true;
-                }
+                // the next segment's first stage, into buffer 1
+                issue_part(1, 0, 0, NDMA);
+                pre = true;
             }
             finish(ctile, cks, cke, em0, en0);
             // the epilogue stages through buffer 0 without a closing barrier;

@@ -371,33 +371,6 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile(const MfmaAr
     }
 }
 
-// Epilogue of a tile held as 32x32 accumulator blocks: lane l holds rows
-// 8 (r / 4) + 4 (l / 32) + r % 4, r = 0..15, of column l % 32.  32-row
-// strips, stg: NW x 32 x (WTN + 8) fp32 (the pad puts the two row halves a
-// lane group writes in different banks).
-template <int DT, int BM, int BN, int WM, int WN, int MODE, int TM, int TN>
-__device__ __attribute__((always_inline)) inline void epilogue_tile32(const MfmaArgs& p, f32x16 (&acc)[TM][TN], float* stg_all,
-                                       int m0, int n0, int split) {
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    static_assert(TM * 32 == WTM && TN * 32 == WTN, "wave tile");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
-    constexpr int PITCH = WTN + 8;
-    float* stg = stg_all + wave * (32 * PITCH);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                stg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * j + (lane & 31)] =
-                    acc[i][j][r];
-        __syncthreads();
-        drain_strip<DT, MODE, WTN, 32, PITCH>(p, stg, m0 + wm0 + 32 * i, n0 + wn0, split, lane);
-        __syncthreads();
-    }
-}
-
 template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MODE>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_mfma_kernel(MfmaArgs p) {
     constexpr int NT = WM * WN * 64;
