@@ -324,3 +324,33 @@ def test_skinny_kernel(M, N, K, trans_b, dtype):
                     algo="skinny")
         torch.cuda.synchronize()
         assert_close(C, T, U, 1.25, beta, cold, bias if epi != "none" else None, what=epi)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("out", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_direct_lds_path_epilogue_every_output(out, trans_b, dtype):
+    # the direct kernels' register epilogue (each lane: 4 consecutive
+    # columns of a row; 16-bit outputs repacked through the wave's LDS):
+    # alpha, beta reading C, bias and GELU for every tile and output type
+    M, N, K = 512, 512, 256
+    A, B = _operands(M, N, K, dtype, trans_b, False, 900)
+    r = np.random.Generator(np.random.PCG64(901))
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), dtype)
+    bias = oracle.decode(bias_bits, dtype)
+    out_name = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[out]
+    cold_bits = inputs.to_bits(r.uniform(-1, 1, (M, N)), out_name)
+    cold = oracle.decode(cold_bits, out_name)
+    for epi, beta in (("bias_gelu", -0.5), ("bias", 0.0), ("none", 1.0)):
+        b = bias if epi != "none" else None
+        T, U = oracle.gemm(A, B, dtype, trans_b=trans_b, alpha=0.75, beta=beta, C_old=cold,
+                           epi=epi, bias=b)
+        for tile in DIRECT_TILES:
+            if tile == "128x64" and not trans_b:
+                continue  # runs the register-staged kernel
+            C = to_dev(cold_bits, out_name)
+            dge.gemm_ex(to_dev(A, dtype), to_dev(B, dtype), C, trans_b=trans_b, alpha=0.75,
+                        beta=beta, epi=epi, bias=to_dev(bias_bits, dtype) if b is not None else None,
+                        algo="mfma_direct", tile=tile, splits=1)
+            torch.cuda.synchronize()
+            assert_close(C, T, U, 0.75, beta, cold, b, what="%s %s beta=%g" % (tile, epi, beta))
