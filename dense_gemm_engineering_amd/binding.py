@@ -20,7 +20,7 @@ OUT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 IN = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
 ALGO = {"auto": 0, "naive": 1, "lds_tiled": 2, "mfma": 3, "mfma_direct": 4, "skinny": 5,
         "decode": 6, "streamk": 7}
-TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x256w8": 5}
+TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x256w8": 5, "256x128w8": 6}
 QTYPE = {"q4_0": 0, "q4_k": 1, "q6_k": 2, "q6_k_224": 3}
 
 # Every symbol include/gemm.h declares.

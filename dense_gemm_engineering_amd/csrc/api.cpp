@@ -163,12 +163,14 @@ int env_int(const char* name, int dflt) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Per-CU MFMA throughput of each tile configuration with the chip full,
-// relative to the 8-wave 256 x 256 tile (measured on MI355X at 4096^3, fp16,
-// direct-to-LDS path): one wave per SIMD cannot keep the MFMA pipe busy,
-// so the 4-wave 256-wide tiles lag; 128 x 128 runs two workgroups per CU.
+// Workgroups of a tile that run on one CU at once: the 256-row tiles' two
+// LDS stages (96 or 128 KB) leave room for one; 128 x 128 and 128 x 64 run
+// two.
 int tile_occupancy(int tile) {
-    return tile == TILE_256x256 || tile == TILE_256x128 || tile == TILE_256x256_W8 ? 1 : 2;
+    return tile == TILE_256x256 || tile == TILE_256x128 || tile == TILE_256x256_W8 ||
+                   tile == TILE_256x128_W8
+               ? 1
+               : 2;
 }
 
 // Time model of one round (every CU running tile_occupancy tiles at once) of
@@ -176,7 +178,9 @@ int tile_occupancy(int tile) {
 // Calibrated on 16-bit 4096^3 and 2048 x {4096, 11008} x {4096, 11008}
 // products with the direct-to-LDS kernels (4096^3: the 8-wave 256 x 256 tile
 // takes ~116 us, the 4-wave one ~130 us, 256 x 128 and 128 x 128 ~146-151 us
-// over two rounds).
+// over two rounds); the 8-wave 256 x 128 tile on 2048 x 4096 x K, K = 1024
+// .. 11008 (one round: 24.0, 37.3, 64.6, 120.3, 160.2 us for K = 1024, 2048,
+// 4096, 8192, 11008).
 struct TileCost {
     double fixed_us, us_per_k;
 };
@@ -185,6 +189,7 @@ TileCost tile_cost(int tile) {
         case TILE_256x256_W8: return {15.0, 0.0246};
         case TILE_256x256: return {17.0, 0.0276};
         case TILE_256x128: return {10.0, 0.0160};
+        case TILE_256x128_W8: return {9.0, 0.0136};
         case TILE_128x128: return {10.0, 0.0160};
         default: return {8.0, 0.0110};  // 128 x 64
     }
@@ -615,7 +620,7 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
     gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
     if (tuning) tn = *tuning;
     if (tn.algo < GEMM_ALGO_AUTO || tn.algo > GEMM_ALGO_STREAMK) return GEMM_ERR_INVALID_VALUE;
-    if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8) return GEMM_ERR_INVALID_VALUE;
+    if (tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x128_W8) return GEMM_ERR_INVALID_VALUE;
     if (tn.splits < 0) return GEMM_ERR_INVALID_VALUE;
     if (g.M == 0 || g.N == 0) return GEMM_OK;
     if ((st = forced_failure()) != GEMM_OK) return st;
@@ -813,7 +818,7 @@ gemm_status_t gemm_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_
     gemm_tuning_t tn{GEMM_ALGO_AUTO, GEMM_TILE_AUTO, 0};
     if (tuning) tn = *tuning;
     if ((tn.algo != GEMM_ALGO_AUTO && tn.algo != GEMM_ALGO_MFMA_DIRECT) ||
-        tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x256_W8 || tn.splits < 0)
+        tn.tile < GEMM_TILE_AUTO || tn.tile > GEMM_TILE_256x128_W8 || tn.splits < 0)
         return GEMM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return GEMM_ERR_INVALID_VALUE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_VALUE;

@@ -21,6 +21,7 @@ hipError_t launch_mfma_q4_f16(int tile, const MfmaArgs& a, int nwg, hipStream_t 
         case TILE_128x128: return launch_q4_one<128, 128, 2, 2>(a, nwg, s);
         case TILE_128x64: return launch_q4_one<128, 64, 2, 2>(a, nwg, s);
         case TILE_256x256_W8: return launch_q4_one<256, 256, 2, 4>(a, nwg, s);
+        case TILE_256x128_W8: return launch_q4_one<256, 128, 4, 2>(a, nwg, s);
         default: return hipErrorInvalidValue;
     }
 }

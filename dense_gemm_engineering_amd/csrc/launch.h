@@ -14,7 +14,7 @@ namespace dge {
 
 // Tile configurations (values match gemm_tile_t).
 enum : int { TILE_256x256 = 1, TILE_256x128 = 2, TILE_128x128 = 3, TILE_128x64 = 4,
-              TILE_256x256_W8 = 5, TILE_LAST = 5 };
+              TILE_256x256_W8 = 5, TILE_256x128_W8 = 6, TILE_LAST = 6 };
 
 struct TileShape {
     int bm, bn;
@@ -25,6 +25,7 @@ inline TileShape tile_shape(int tile) {
         case TILE_256x128: return {256, 128};
         case TILE_128x128: return {128, 128};
         case TILE_256x256_W8: return {256, 256};
+        case TILE_256x128_W8: return {256, 128};
         default: return {128, 64};
     }
 }

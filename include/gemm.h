@@ -152,7 +152,9 @@ typedef enum {
     GEMM_TILE_256x128 = 2, /* 4 waves, 128 x 64 per wave */
     GEMM_TILE_128x128 = 3, /* 4 waves, 64 x 64 per wave */
     GEMM_TILE_128x64 = 4,  /* 4 waves, 64 x 32 per wave */
-    GEMM_TILE_256x256_W8 = 5 /* 8 waves (two per SIMD), 128 x 64 per wave */
+    GEMM_TILE_256x256_W8 = 5, /* 8 waves (two per SIMD), 128 x 64 per wave */
+    GEMM_TILE_256x128_W8 = 6  /* 8 waves (4 x 2), 64 x 64 per wave; the register-staged
+                                 family runs it as GEMM_TILE_256x128 */
 } gemm_tile_t;
 
 typedef struct {

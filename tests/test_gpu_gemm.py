@@ -17,7 +17,7 @@ from gpu_util import assert_bits, assert_close, to_dev, bits_of
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "256x128", "128x128", "128x64", "256x256w8"]
+TILES = ["256x256", "256x128", "128x128", "128x64", "256x256w8", "256x128w8"]
 
 
 def _operands(M, N, K, dtype, trans_b, integer, seed):
@@ -251,7 +251,7 @@ def test_forced_launch_failure(monkeypatch):
     assert torch.all(C == 8)
 
 
-DIRECT_TILES = ["256x256w8", "256x256", "256x128", "128x128", "128x64"]
+DIRECT_TILES = ["256x256w8", "256x128w8", "256x256", "256x128", "128x128", "128x64"]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

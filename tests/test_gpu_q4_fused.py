@@ -19,7 +19,7 @@ from gpu_util import assert_bits, assert_close, bits_of, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
-FUSED_TILES = ["256x256w8", "256x256", "256x128", "128x128", "128x64"]
+FUSED_TILES = ["256x256w8", "256x128w8", "256x256", "256x128", "128x128", "128x64"]
 
 
 def _q(q):

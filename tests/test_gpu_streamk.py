@@ -20,7 +20,7 @@ from gpu_util import assert_bits, assert_close, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256w8", "256x256", "256x128", "128x128", "128x64"]
+TILES = ["256x256w8", "256x128w8", "256x256", "256x128", "128x128", "128x64"]
 
 
 def _ws(M, N, K, tile="auto"):
