@@ -80,7 +80,7 @@ __device__ inline void skinny_load4(const SkinnyArgs& p, int m, int n0, float* t
 // Epilogue of one wave's RB x 16 rows starting at row base: alpha/beta,
 // bias, GELU and rounding in registers (4 consecutive columns per lane), the
 // rounded values staged in the wave's LDS tile (rows of pitch_o bytes), then
-// written out row by row with 16-byte stores so that a wave writes whole
+// written out row by row with 16-byte non-temporal stores so that a wave writes whole
 // rows of C.
 template <int OT, int NT, int RB>
 __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB][NT],
@@ -134,7 +134,7 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB]
             const char* src = stage + r * pitch_o + c * 16;
             char* dst = (char*)p.C + ((int64_t)mm * p.ldc) * OB + c * 16;
             if (vec) {
-                *(u32x4*)dst = *(const u32x4*)src;
+                __builtin_nontemporal_store(*(const u32x4*)src, (u32x4*)dst);
             } else {
                 for (int e = 0; e < 16 / OB; ++e)
                     if (c * 16 + e * OB < row_bytes) ((T*)dst)[e] = ((const T*)src)[e];
