@@ -53,9 +53,11 @@
 //    counter can track 15 outstanding reads, so they are issued a few at a
 //    time between MFMAs); the barrier sits before the last MFMAs of a stage,
 //    and right after it each wave issues the first part of the direct loads
-//    two stages ahead and the first reads of the next stage, so the MFMA
-//    pipe keeps busy across the barrier; the rest of those loads go out
-//    between the MFMAs of the following k-blocks.
+//    two stages ahead and the first reads of the next stage, one load and
+//    its share of the reads per remaining MFMA (not as a burst: 4096^3 NN
+//    109.8 -> 109.1 us, NT 108.7 -> 107.6 us), so the MFMA pipe keeps busy
+//    across the barrier; the rest of those loads go out between the MFMAs of
+//    the following k-blocks.
 #pragma once
 
 #include "mfma_gemm.h"
@@ -122,6 +124,18 @@ __device__ inline void interleave_reads() {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);  // m MFMAs
         interleave_reads<NRD, NMF, R + 1>();
+    }
+}
+
+// Scheduling pattern of a stage's last NM MFMAs after the barrier: each MFMA
+// followed by its share of the NRD fragment reads of the next k-block.
+template <int NM, int NRD, int R = 0>
+__device__ inline void tail_reads() {
+    if constexpr (R < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        constexpr int n = (R + 1) * NRD / NM - R * NRD / NM;
+        if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // n LDS reads
+        tail_reads<NM, NRD, R + 1>();
     }
 }
 
@@ -462,16 +476,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // ---- fragment reads of k-block kb
     // A (and K-contiguous B): row r = base + (lane % MS), chunk
     // (CPK kb + lane / MS) ^ swz_k(r) (the same swizzle for every block of rows).
-    auto read_rows = [&](const DGE_LDS char* base, int row0, int kb, int ntile, u32x4* f) __attribute__((always_inline)) {
+    // (lo, hi: only reads lo .. hi - 1 of the ones listed, for spreading a
+    // k-block's reads over several MFMAs)
+    auto read_rows = [&](const DGE_LDS char* base, int row0, int kb, int ntile, u32x4* f,
+                         int lo = 0, int hi = 1 << 20) __attribute__((always_inline)) {
         const int r = row0 + (lane % MS);
         const DGE_LDS char* q = base + r * 128 + (((kb * CPK + lane / MS) ^ swz_k<MS>(r)) << 4);
 #pragma unroll
-        for (int i = 0; i < ntile; ++i) f[i] = *(const DGE_LDS u32x4*)(q + i * MS * 128);
+        for (int i = 0; i < ntile; ++i)
+            if (i >= lo && i < hi) f[i] = *(const DGE_LDS u32x4*)(q + i * MS * 128);
     };
     // K x N B via transposed reads.  Lane group g = lane / 16 covers k-rows
     // kb KBLK + 8 (g / (MS / 16)) + 4 h + (t / 4) and columns
     // wn0 + MS j + 16 (g % (MS / 16)) + 4 (t % 4).
-    auto read_bt = [&](const DGE_LDS char* base, int kb, u32x4* f) __attribute__((always_inline)) {
+    auto read_bt = [&](const DGE_LDS char* base, int kb, u32x4* f, int lo = 0,
+                       int hi = 1 << 20) __attribute__((always_inline)) {
         const int t = lane & 15, g = lane >> 4;
         const int kofs = MS == 16 ? 8 * g : 8 * (g >> 1);
         const int nofs = MS == 16 ? 0 : 16 * (g & 1);
@@ -482,6 +501,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             const DGE_LDS char* rowp = base + k * (BN * 2);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
+                if (h * TN + j < lo || h * TN + j >= hi) continue;
                 const int n = nloc + MS * j;
                 const int c = (n >> 3) ^ swz_b<MS>(k);
                 const uint2 v = ds_read_tr(rowp + (c << 4) + ((n & 7) << 1));
@@ -504,14 +524,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     };
 
     u32x4 fa[2][TM], fb[2][TN];
-    auto read_kblock = [&](int st, int kb, u32x4* a, u32x4* b) __attribute__((always_inline)) {
+    // reads lo .. hi - 1 of k-block kb's fragment reads (A's TM first, then B's)
+    auto read_kblock = [&](int st, int kb, u32x4* a, u32x4* b, int lo = 0,
+                           int hi = 1 << 20) __attribute__((always_inline)) {
         const DGE_LDS char* la = (const DGE_LDS char*)&lds[st][0];
         const DGE_LDS char* lb = (const DGE_LDS char*)&lds[st][A_BYTES];
-        read_rows(la, wm0, kb, TM, a);
+        read_rows(la, wm0, kb, TM, a, lo, hi);
         if constexpr (TRANS_B)
-            read_rows(lb, wn0, kb, TN, b);
+            read_rows(lb, wn0, kb, TN, b, lo - TM, hi - TM);
         else
-            read_bt(lb, kb, b);
+            read_bt(lb, kb, b, lo - TM, hi - TM);
     };
     // MFMAs [lo, hi) of one k-block over the TM x TN blocks in serpentine
     // order (row i left to right, row i + 1 right to left), so consecutive
@@ -601,15 +623,29 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage kt + 1
         __syncthreads();
 
-        issue_part(st, min(kt + 2, nk - 1), 0, NP0);
-        if constexpr (Q4) q4_load(min(kt + 2, nk - 1));
-        read_kblock(st ^ 1, 0, fa[0], fb[0]);
-        mma_range(fa[L], fb[L], NMF - TAIL, NMF);
+        if constexpr (Q4) {
+            issue_part(st, min(kt + 2, nk - 1), 0, NP0);
+            q4_load(min(kt + 2, nk - 1));
+            read_kblock(st ^ 1, 0, fa[0], fb[0]);
+            mma_range(fa[L], fb[L], NMF - TAIL, NMF);
 #pragma unroll
-        for (int r = 0; r < TAIL; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x020, (NDMA + TAIL - 1) / TAIL, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, (NRD + TAIL - 1) / TAIL, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int r = 0; r < TAIL; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x100, (NRD + TAIL - 1) / TAIL, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        } else {
+            // the direct loads and the next k-block's reads in TAIL steps, each
+            // after one of the last MFMAs: the matrix unit restarts right
+            // after the barrier instead of after a burst of loads (the loads
+            // are ordered with the LDS reads in program order, so the steps
+            // are written out one by one)
+#pragma unroll
+            for (int r = 0; r < TAIL; ++r) {
+                issue_part(st, min(kt + 2, nk - 1), r * NP0 / TAIL, (r + 1) * NP0 / TAIL);
+                read_kblock(st ^ 1, 0, fa[0], fb[0], r * NRD / TAIL, (r + 1) * NRD / TAIL);
+            }
+            mma_range(fa[L], fb[L], NMF - TAIL, NMF);
+            tail_reads<TAIL, NRD>();
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
