@@ -7,8 +7,10 @@
 //    back to back keeps its SIMD's matrix unit ~98% busy on gfx950, one
 //    wave of 16x16x32 MFMAs only ~60% (two waves per SIMD ~91%).  So the
 //    4-wave tiles (one wave per SIMD) use 32x32x16 blocks (MS = 32); the
-//    8-wave 256 x 256 tile, with two waves per SIMD, measured faster with
-//    16x16x32 blocks (MS = 16: 119 vs 124 us at 4096^3, K x N B).
+//    8-wave tiles (256 x 256 as 2 x 4 waves, 256 x 128 as 4 x 2), with two
+//    waves per SIMD, measured faster with 16x16x32 blocks (MS = 16: 119 vs
+//    124 us at 4096^3, K x N B; 2048 x 4096 x 4096 with 256 x 128 tiles
+//    64.6 us against 70.4 for the 4-wave 32x32x16 tile).
 //    Operand layouts: lane l supplies row (l % MS) of A and column (l % MS)
 //    of B, each with 8 consecutive k (chunk l / MS of the k-block, which is
 //    32 deep for MS = 16 and 16 deep for MS = 32).  A 16x16 block gives lane
