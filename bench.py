@@ -131,13 +131,39 @@ def time_graph(fn, steps, torch, warm_seconds=0.3, reps=5):
     return t
 
 
+def _strip_comments(src):
+    """C/C++ source without its comments and blank lines (string and
+    character literals kept), so that comment edits leave the hash alone."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (l.rstrip() for l in "".join(out).split("\n"))
+    return "\n".join(l for l in lines if l)
+
+
 def _src_hash():
+    """Hash of the kernel and library sources, comments left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_engineering_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".h", ".hip", ".cpp", ".inc")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                h.update(f.encode() + _strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -45,3 +45,9 @@ def test_alg_bytes_and_dequant_bytes():
 def test_stack_tokens_per_s():
     assert bench.prefill_stack_tokens_per_s(1e-6, 2e-6, 3e-6) == pytest.approx(
         2048 / (32 * (4e-6 + 4e-6 + 3e-6)))
+
+
+def test_source_hash_ignores_comments_only():
+    src = 'int a = 1; // note\n/* block\n comment */ const char* s = "x // y"; char q = \'"\';\n'
+    assert bench._strip_comments(src) == 'int a = 1;\n const char* s = "x // y"; char q = \'"\';'
+    assert bench._strip_comments("a /* x */ + b // y\n") == "a  + b"
