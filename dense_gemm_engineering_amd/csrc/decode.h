@@ -8,7 +8,9 @@
 //    K into 8 slices of whole 32-deep k-blocks.  Within a wave, the MFMA "A"
 //    operand is 8 consecutive k of one weight row per lane, i.e. a 16-byte
 //    load straight from W into registers (no LDS), and the "B" operand is 8
-//    consecutive k of one row of X (L2-resident: X is at most 64 x K).  The
+//    consecutive k of one row of X (L2-resident: X is at most 64 x K; for
+//    M > 1 loaded with whole 64-byte row pieces per lane quad and moved
+//    into the operand layout through a small per-wave LDS slot).  The
 //    product is C^T = W X^T in 16 x 16 blocks, MT = ceil(M / 16) of them.
 //  * Loads for 16 k-blocks (8 for M > 32) are issued before their MFMAs, so
 //    each lane keeps up to 256 bytes of W (and of X) in flight; with 8 waves
@@ -39,25 +41,39 @@ constexpr int DECODE_WAVES = 8;
 // trip per wave) while the registers allow, 8 for M > 32
 __host__ __device__ constexpr int decode_batch(int mt) { return mt <= 2 ? 16 : 8; }
 
-template <int DT, int MT>
+// XT: X goes through the per-wave transpose slot (below); off for M = 1,
+// whose clamped rows make every quad read one address anyway.
+template <int DT, int MT, bool XT = true>
 __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeArgs p) {
     // partial C^T blocks of every wave: [wave][mt][16 n][16 m] fp32
     __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][MT][256];
+    // each wave's X transpose slot: MT blocks of 16 rows x 4 16-byte chunks
+    __shared__ __attribute__((aligned(16))) u32x4 xslot[XT ? DECODE_WAVES : 1][MT][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * 16;
     const int nkb = (p.K + 31) / 32;
     const int kb0 = wave * nkb / DECODE_WAVES, kb1 = (wave + 1) * nkb / DECODE_WAVES;
 
-    // this lane's rows: weight row n0 + (lane & 15) (clamped to the last row:
-    // valid memory, never stored), input rows 16 mt + (lane & 15) (clamped)
+    // this lane's weight row: n0 + (lane & 15) (clamped to the last row:
+    // valid memory, never stored); input rows are clamped to M - 1 the same way
     const int nr = min(n0 + (lane & 15), p.N - 1);
     const char* wrow = (const char*)p.W + ((int64_t)nr * p.ldw + 8 * (lane >> 4)) * 2;
+    // X is loaded with the four lanes of a quad on one row's 64 contiguous
+    // bytes (lane L: row 16 mt + L / 4, chunk L % 4): in the MFMA operand
+    // layout (row L % 16) every quad would touch four rows, and the address
+    // unit spends a cycle per row (M = 64: 24.4 -> 19.1 us for the loads
+    // alone).  Each k-block's X then goes through the wave's LDS slot into
+    // the operand layout; chunk c of row r sits at r * 4 + (c ^ ((r >> 2) & 3)),
+    // so the sixteen rows of one chunk fall in different bank groups.
+    const int xrl = XT ? lane >> 2 : lane & 15, xcl = XT ? lane & 3 : lane >> 4;  // row, chunk
     const char* xrow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int mr = min(16 * mt + (lane & 15), p.M - 1);
-        xrow[mt] = (const char*)p.X + ((int64_t)mr * p.ldx + 8 * (lane >> 4)) * 2;
+        const int mr = min(16 * mt + xrl, p.M - 1);
+        xrow[mt] = (const char*)p.X + ((int64_t)mr * p.ldx + 8 * xcl) * 2;
     }
+    const int xw = 4 * (lane >> 2) + ((lane & 3) ^ ((lane >> 4) & 3));  // where this lane's load goes
+    const int xr = 4 * (lane & 15) + ((lane >> 4) ^ ((lane >> 2) & 3));  // where its operand comes from
     const int kchunk = 8 * (lane >> 4);  // this lane's k offset within a k-block
 
     f32x4 acc[MT];
@@ -69,17 +85,34 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
         u32x4 wf[DECODE_BATCH], xf[DECODE_BATCH][MT];
 #pragma unroll
         for (int i = 0; i < DECODE_BATCH; ++i) {
-            const int k = (kb + i) * 32 + kchunk;
-            const bool in = kb + i < kb1 && k < p.K;  // K % 8 == 0: a chunk is all in or all out
+            // K % 8 == 0: a chunk is all in or all out (W and X lanes hold
+            // different chunks, each masked by its own k)
+            const int k = (kb + i) * 32 + kchunk, kx = (kb + i) * 32 + 8 * xcl;
+            const bool in = kb + i < kb1 && k < p.K, inx = kb + i < kb1 && kx < p.K;
             wf[i] = in ? load16(wrow + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                xf[i][mt] = in ? load16(xrow[mt] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+                xf[i][mt] = inx ? load16(xrow[mt] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < DECODE_BATCH; ++i)
+        for (int i = 0; i < DECODE_BATCH; ++i) {
+            // the wave's own LDS operations complete in order: the reads see
+            // these writes, and the next k-block's writes land after them
+            u32x4 xo[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[mt], wf[i], xf[i][mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+                if constexpr (XT)
+                    xslot[wave][mt][xw] = xf[i][mt];
+                else
+                    xo[mt] = xf[i][mt];
+            }
+            if constexpr (XT) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) xo[mt] = xslot[wave][mt][xr];
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[mt], wf[i], xo[mt]);
+        }
     }
 
     // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each block

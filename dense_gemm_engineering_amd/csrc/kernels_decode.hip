@@ -8,7 +8,12 @@ template <int DT>
 static hipError_t decode_dt(const DecodeArgs& a, int grid, hipStream_t s) {
     const dim3 block(DECODE_WAVES * 64);
     switch ((a.M + 15) / 16) {
-        case 1: hipLaunchKernelGGL((gemm_decode_kernel<DT, 1>), dim3(grid), block, 0, s, a); break;
+        case 1:
+            if (a.M == 1)
+                hipLaunchKernelGGL((gemm_decode_kernel<DT, 1, false>), dim3(grid), block, 0, s, a);
+            else
+                hipLaunchKernelGGL((gemm_decode_kernel<DT, 1>), dim3(grid), block, 0, s, a);
+            break;
         case 2: hipLaunchKernelGGL((gemm_decode_kernel<DT, 2>), dim3(grid), block, 0, s, a); break;
         case 3: hipLaunchKernelGGL((gemm_decode_kernel<DT, 3>), dim3(grid), block, 0, s, a); break;
         case 4: hipLaunchKernelGGL((gemm_decode_kernel<DT, 4>), dim3(grid), block, 0, s, a); break;
