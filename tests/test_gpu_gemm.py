@@ -278,12 +278,13 @@ def test_direct_lds_path_split_k_and_epilogue(trans_b):
     Ti, _ = oracle.gemm(Ai, Bi, "f16", trans_b=trans_b)
     ws = torch.empty(dge.gemm_workspace_size_splits(M, N, 3) // 4, dtype=torch.float32,
                      device="cuda")
-    for splits in (2, 3):
-        C = dge.gemm_ex(to_dev(Ai, "f16"), to_dev(Bi, "f16"), trans_b=trans_b,
-                        out_dtype=torch.float32, workspace=ws, algo="mfma_direct",
-                        tile="256x256w8", splits=splits)
-        torch.cuda.synchronize()
-        assert_bits(C, Ti, what="splits=%d" % splits)
+    for tile in ("256x256w8", "256x128w8"):
+        for splits in (2, 3):
+            C = dge.gemm_ex(to_dev(Ai, "f16"), to_dev(Bi, "f16"), trans_b=trans_b,
+                            out_dtype=torch.float32, workspace=ws, algo="mfma_direct",
+                            tile=tile, splits=splits)
+            torch.cuda.synchronize()
+            assert_bits(C, Ti, what="%s splits=%d" % (tile, splits))
     A, B = _operands(M, N, K, "f16", trans_b, False, 801)
     r = np.random.Generator(np.random.PCG64(802))
     bias_bits = inputs.to_bits(r.normal(0, 0.1, N), "f16")

@@ -79,8 +79,9 @@ def test_fused_unit_scales_integer_exact(tile):
     assert_bits(C, T, what=tile)
 
 
+@pytest.mark.parametrize("tile", ["256x256w8", "256x128w8"])
 @pytest.mark.parametrize("splits", [2, 3])
-def test_fused_split_k_exact_and_deterministic(splits):
+def test_fused_split_k_exact_and_deterministic(splits, tile):
     M, N, K = 256, 512, 2048
     q = _unit_scale_q4(N, K, 5200)
     r = np.random.Generator(np.random.PCG64(5201))
@@ -91,9 +92,9 @@ def test_fused_split_k_exact_and_deterministic(splits):
     outs = []
     for _ in range(2):
         C = dge.gemm_q4_f16(to_dev(A, "f16"), _q(q), N, K, out_dtype=torch.float32, workspace=ws,
-                            algo="mfma_direct", tile="256x256w8", splits=splits)
+                            algo="mfma_direct", tile=tile, splits=splits)
         torch.cuda.synchronize()
-        assert_bits(C, T, what="splits=%d" % splits)
+        assert_bits(C, T, what="%s splits=%d" % (tile, splits))
         outs.append(C.cpu())
     assert torch.equal(outs[0], outs[1])
 
