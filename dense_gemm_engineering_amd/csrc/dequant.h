@@ -103,6 +103,10 @@ __global__ __launch_bounds__(256) void dequant_q4_f16_kernel(const uint8_t* __re
 //     dmin m in fp32 (both products exact, the difference rounded once), then
 //     rounded to binary16: two roundings, which differ from one rounding of
 //     the exact value when the binary32 result is a binary16 tie.
+//   q4_0 rows of a multiple of 256 weights (QT = KQ_Q4_0_256) take the same
+//     path as groups of eight 18-byte blocks, 144 bytes per 256 weights:
+//     persistent workgroups with the next group prefetched into registers
+//     move them faster than the one-step-per-workgroup q4_0 kernel above.
 // A workgroup stages SB consecutive super-blocks (SB a multiple of 8: 1680,
 // 1792 or 1152 bytes per 8, multiples of 16) into LDS with coalesced loads; task c
 // then decodes the 16-byte output chunk c % 32 (weights 8 (c % 32) .. + 7) of
@@ -116,6 +120,7 @@ template <int QT> struct KQuant;
 template <> struct KQuant<KQ_Q4_K> { static constexpr int BYTES = 144; static constexpr bool Q6 = false; };
 template <> struct KQuant<KQ_Q6_K> { static constexpr int BYTES = 210; static constexpr bool Q6 = true; };
 template <> struct KQuant<KQ_Q6_K_224> { static constexpr int BYTES = 224; static constexpr bool Q6 = true; };
+template <> struct KQuant<KQ_Q4_0_256> { static constexpr int BYTES = 144; static constexpr bool Q6 = false; };
 
 template <int QT, int SB>
 __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __restrict__ q,
@@ -168,7 +173,21 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
             const uint8_t* blk = raw + BYTES * sbl;
             const int e0 = 8 * c;
             uint16_t h[8];
-            if constexpr (KQuant<QT>::Q6) {
+            if constexpr (QT == KQ_Q4_0_256) {
+                // chunk c % 4 of q4_0 block c / 4 of the group: the low (chunk
+                // < 2) or high nibbles of code bytes 8 (chunk & 1) .. + 7
+                const uint8_t* b = blk + 18 * (c >> 2);
+                const int p = c & 3;
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[0] | (b[1] << 8)));
+                const uint8_t* qs = b + 2 + 8 * (p & 1);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int code = p < 2 ? (qs[i] & 15) : (qs[i] >> 4);
+                    float v = d * (float)(code - 8);  // exact; one rounding below
+                    __asm__("" : "+v"(v));  // a multiply, not a mixed-precision FMA
+                    h[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                }
+            } else if constexpr (KQuant<QT>::Q6) {
                 const int hh = e0 / 128, tt = (e0 % 128) / 32, l0 = e0 % 32;
                 const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[208] | (blk[209] << 8)));
                 const float dsc = d * (float)(int8_t)blk[192 + 8 * hh + 2 * tt + l0 / 16];  // exact

@@ -11,8 +11,10 @@ namespace dge {
 enum : int { IN_F16 = 0, IN_BF16 = 1, IN_F32 = 2 };
 enum : int { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 enum : int { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU = 2 };
-// block-quantised weight formats (numbered as gemm_qtype_t)
-enum : int { KQ_Q4_0 = 0, KQ_Q4_K = 1, KQ_Q6_K = 2, KQ_Q6_K_224 = 3 };
+// block-quantised weight formats (numbered as gemm_qtype_t); KQ_Q4_0_256 is
+// internal: q4_0 rows whose length is a multiple of 256, walked as groups of
+// eight 18-byte blocks (144 bytes per 256 weights)
+enum : int { KQ_Q4_0 = 0, KQ_Q4_K = 1, KQ_Q6_K = 2, KQ_Q6_K_224 = 3, KQ_Q4_0_256 = 4 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

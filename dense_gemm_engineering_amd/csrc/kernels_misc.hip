@@ -70,6 +70,7 @@ hipError_t launch_clear_u32(unsigned* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
                              int vec_out, hipStream_t s) {
+    if (cols % 256 == 0) return launch_dequant_kq(KQ_Q4_0_256, q, out, rows, cols, ldo, vec_out, s);
     const int64_t total = rows * (cols / 32);
     int64_t blocks = (total + DQ_BLOCKS - 1) / DQ_BLOCKS;
     if (blocks > 1 << 20) blocks = 1 << 20;
@@ -91,6 +92,9 @@ hipError_t launch_dequant_kq(int qtype, const void* q, void* out, int64_t rows, 
     if (qtype == KQ_Q6_K)
         hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q6_K, SB>), dim3((unsigned)blocks), dim3(256), 0,
                            s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
+    else if (qtype == KQ_Q4_0_256)
+        hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q4_0_256, SB>), dim3((unsigned)blocks), dim3(256),
+                           0, s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
     else if (qtype == KQ_Q6_K_224)
         hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q6_K_224, SB>), dim3((unsigned)blocks), dim3(256),
                            0, s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);

@@ -74,6 +74,35 @@ def test_dequant_every_scale_times_every_code():
     assert np.array_equal(g[~np.isnan(g)], w[~np.isnan(w)])
 
 
+def test_dequant_256_wide_rows_every_scale_times_every_code():
+    # rows of 256 weights (eight blocks) take the grouped path: every scale
+    # pattern once, each block holding codes 0..15 and 15..0
+    scales = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(8192, 8)
+    codes = np.empty((8192, 8, 32), dtype=np.uint8)
+    codes[:, :, :16] = np.arange(16)
+    codes[:, :, 16:] = np.arange(15, -1, -1)
+    q = inputs.pack_q4(scales, codes)
+    want = oracle.dequant_q4(q, 8192, 256)
+    got = bits_of(dge.dequant_q4_f16(torch.from_numpy(q).cuda(), 8192, 256))
+    torch.cuda.synchronize()
+    g, w = got.view(np.float16), want.view(np.float16)
+    # bit for bit, any NaN matching any NaN (non-finite scales)
+    assert np.all((got == want) | (np.isnan(g) & np.isnan(w)))
+
+
+@pytest.mark.parametrize("rows,cols,ldo,qoff", [(37, 512, 520, 0), (5, 768, 771, 0),
+                                                (9, 256, 256, 2), (300, 1024, 1024, 16)])
+def test_dequant_grouped_path_strided_and_unaligned(rows, cols, ldo, qoff):
+    q = inputs.q4_weights(rows, cols, 4, 93 + rows)
+    buf = torch.zeros(q.size + qoff, dtype=torch.uint8, device="cuda")
+    buf[qoff:] = torch.from_numpy(q).cuda()
+    out = torch.full((rows, ldo), float("nan"), dtype=torch.float16, device="cuda")
+    dge.dequant_q4_f16(buf[qoff:], rows, cols, out=out[:, :cols])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(out[:, :cols]), oracle.dequant_q4(q, rows, cols))
+    assert torch.all(torch.isnan(out[:, cols:]))
+
+
 @pytest.mark.parametrize("shape", ["up", "attn", "down"])
 def test_dequant_full_size_bit_exact(shape):
     N, K = inputs.PREFILL_SHAPES[shape]
