@@ -568,7 +568,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // for all outstanding loads and must not meet fresh ones)
     constexpr int DPART = Q4 ? 1 : (KB - 1 < 3 ? KB - 1 : 3);
     constexpr int NP0 = NDMA / DPART;                    // loads in the first part
-    constexpr int TAIL = NMF / (MS == 16 ? 4 : 2) > 0 ? NMF / (MS == 16 ? 4 : 2) : 1;  // after the barrier
+    // MFMAs of a stage's last k-block left after the barrier (measured, same
+    // box, alternating processes): the 256 x 256 8-wave tile runs 4096^3 in
+    // 105.7 us with 24 of its 32 after the barrier against 112.3 with 8 (NN;
+    // NT 110.5 -> 104.5), while the 256 x 128 8-wave tile (16 per k-block)
+    // is 1-3% slower with more than 4 there; the fused q4 kernel keeps a
+    // quarter (its decode runs between the MFMAs before the barrier)
+    constexpr int TAIL = MS == 16 ? (!Q4 && NMF >= 32 ? NMF * 3 / 4 : NMF / 4)
+                                  : (NMF / 2 > 0 ? NMF / 2 : 1);
 
     // Main loop over the nk stages of the current tile, stage kt in buffer
     // (kt + par) & 1; pre: stage 0's loads into buffer par are already in
@@ -622,7 +629,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         // drift past it, leaving the matrix unit idle while the wave waits)
         __builtin_amdgcn_sched_barrier(0);
 
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage kt + 1
+        // vmcnt(0): this wave's loads of stage kt + 1 have landed; lgkmcnt(0):
+        // its fragment reads of this stage are done before the barrier lets
+        // other waves load into this buffer (whatever MFMAs precede it)
+        __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
 
         if constexpr (Q4) {
