@@ -505,7 +505,9 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
                      (g.ldc * out_bytes(g.c_type)) % 16 == 0;
     a.vec_ok = vec ? 1 : 0;
     a.ep = make_epilogue(g);
-    const bool fast = vec && g.M % ts.bm == 0 && g.N % ts.bn == 0 && g.K % bk == 0 &&
+    // (K = 0 takes the bounds-checked loads: the unchecked kernels load their
+    // first stages before looking at the stage count)
+    const bool fast = vec && g.K > 0 && g.M % ts.bm == 0 && g.N % ts.bn == 0 && g.K % bk == 0 &&
                       (splits == 1 || a.k_per_split % bk == 0);
     const int64_t nwg = (int64_t)a.tiles_m * a.tiles_n * splits;
     if (nwg > 0x7fffffff) return GEMM_ERR_NOT_SUPPORTED;

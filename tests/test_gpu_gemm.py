@@ -183,6 +183,25 @@ def test_k_zero_is_beta_c_plus_bias():
     assert_bits(C, T)
 
 
+@pytest.mark.parametrize("trans_b", [False, True])
+def test_k_zero_full_tiles(trans_b):
+    # M and N multiples of every tile: K = 0 must not reach the kernels that
+    # load their first K stages unchecked
+    M, N = 512, 512
+    r = np.random.Generator(np.random.PCG64(301))
+    cold_bits = inputs.to_bits(r.uniform(-1, 1, (M, N)), "f32")
+    bias_bits = inputs.to_bits(r.uniform(-1, 1, N), "f16")
+    C = to_dev(cold_bits, "f32")
+    A = torch.empty((M, 0), dtype=torch.float16, device="cuda")
+    B = torch.empty((N, 0) if trans_b else (0, N), dtype=torch.float16, device="cuda")
+    dge.gemm_f16(A, B, C, trans_b=trans_b, beta=-1.0, epi="bias", bias=to_dev(bias_bits, "f16"))
+    torch.cuda.synchronize()
+    T, _ = oracle.gemm(np.zeros((M, 0), np.uint16), np.zeros((N, 0) if trans_b else (0, N), np.uint16),
+                       "f16", trans_b=trans_b, beta=-1.0, C_old=oracle.decode(cold_bits, "f32"),
+                       epi="bias", bias=oracle.decode(bias_bits, "f16"))
+    assert_bits(C, T)
+
+
 def test_empty_m_or_n_is_a_no_op():
     A = torch.empty((0, 64), dtype=torch.float16, device="cuda")
     B = torch.ones((64, 32), dtype=torch.float16, device="cuda")

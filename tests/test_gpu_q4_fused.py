@@ -133,6 +133,21 @@ def test_fused_bias_gelu_epilogue():
     assert_close(C, T, U, bias=bias)
 
 
+def test_fused_k_zero_full_tiles_is_the_bias():
+    # K = 0 with M and N multiples of every tile: no weights, C = bias (beta
+    # is 0 here); nothing may load a first K stage
+    M, N = 512, 512
+    r = np.random.Generator(np.random.PCG64(5500))
+    bias_bits = inputs.to_bits(r.uniform(-1, 1, N), "f16")
+    A = torch.empty((M, 0), dtype=torch.float16, device="cuda")
+    q = torch.empty(0, dtype=torch.uint8, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    dge.gemm_q4_f16(A, q, N, 0, C, epi="bias", bias=to_dev(bias_bits, "f16"))
+    torch.cuda.synchronize()
+    want = np.broadcast_to(oracle.decode(bias_bits, "f16").astype(np.float32), (M, N))
+    assert np.array_equal(C.cpu().numpy(), want)
+
+
 def test_fused_ragged_shape_falls_back_through_the_workspace():
     # M, N not multiples of any tile: the weights are expanded into the workspace
     M, N, K = 33, 70, 256
