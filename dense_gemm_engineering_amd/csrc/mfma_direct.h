@@ -356,7 +356,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int RPI_B = 1024 / (BN * 2);    // k-rows per 1 KB direct-load instruction
     static_assert(TRANS_B || RPI_B * BN * 2 == 1024, "whole k-rows per instruction");
 
-    __shared__ __attribute__((aligned(1024))) char lds[2][A_BYTES + B_BYTES];
+    // LDS stages: a third one where it fits (the 8-wave 256 x 128 tile, 144 KB)
+    // on the plain path, so each stage's loads have two stages to land
+    constexpr int NBUF = (!Q4 && !SK && MS == 16 && NW == 8 &&
+                          3 * (A_BYTES + B_BYTES) <= 160 * 1024) ? 3 : 2;
+    __shared__ __attribute__((aligned(1024))) char lds[NBUF][A_BYTES + B_BYTES];
     __shared__ int sk_flag;  // stream-K: a counter value broadcast to the workgroup
 
     const int tid = threadIdx.x;
@@ -664,6 +668,48 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     __syncthreads();
     };
 
+    // Main loop over three LDS stages (NBUF = 3): stage kt in buffer kt % 3.
+    // The barrier that ends stage kt needs only stage kt + 1 landed (the
+    // loads of stage kt + 2, issued a stage later, stay in flight:
+    // vmcnt(NDMA)); after it the loads of stage kt + 3 go into buffer kt % 3,
+    // one per remaining MFMA, with the reads of stage kt + 1's k-block 0.
+    auto mainloop3 = [&](int nk) __attribute__((always_inline)) {
+    issue_part(0, 0, 0, NDMA);
+    issue_part(1, nk > 1 ? 1 : nk - 1, 0, NDMA);
+    issue_part(2, nk > 2 ? 2 : nk - 1, 0, NDMA);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14)));  // vmcnt(2 NDMA)
+    __syncthreads();
+    read_kblock(0, 0, fa[0], fb[0]);
+    int st = 0;  // buffer of stage kt
+    for (int kt = 0; kt < nk; ++kt) {
+        const int sn = st == NBUF - 1 ? 0 : st + 1;  // buffer of stage kt + 1
+#pragma unroll
+        for (int kb = 0; kb < KB - 1; ++kb) {
+            read_kblock(st, kb + 1, fa[(kb + 1) & 1], fb[(kb + 1) & 1]);
+            mma_range(fa[kb & 1], fb[kb & 1], 0, NMF);
+            interleave_reads<NRD, NMF>();
+        }
+        constexpr int L = (KB - 1) & 1;
+        mma_range(fa[L], fb[L], 0, NMF - TAIL);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - TAIL, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // vmcnt(NDMA): stage kt + 1 has landed (stage kt + 2 may not have);
+        // lgkmcnt(0): this wave's reads of buffer st are done
+        __builtin_amdgcn_s_waitcnt(0x0070 | ((NDMA & 15) | ((NDMA >> 4) << 14)));
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < TAIL; ++r) {
+            issue_part(st, min(kt + 3, nk - 1), r * NDMA / TAIL, (r + 1) * NDMA / TAIL);
+            read_kblock(sn, 0, fa[0], fb[0], r * NRD / TAIL, (r + 1) * NRD / TAIL);
+        }
+        mma_range(fa[L], fb[L], NMF - TAIL, NMF);
+        tail_reads<TAIL, NRD>();
+        st = sn;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    };
+
     // the fused epilogue of tile (em0, en0), staged through buffer 0
     auto epilogue = [&](int em0, int en0, int split) __attribute__((always_inline)) {
         epilogue_tile_t<DT, BM, BN, WM, WN, MS, TM, TN, A_BYTES + B_BYTES>(
@@ -680,7 +726,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         const int k0 = split * p.k_per_split;
         start_tile(tm * BM, tn * BN, k0);
         zero_acc();
-        mainloop((min(k0 + p.k_per_split, p.K) - k0) / BK, 0, false);
+        if constexpr (NBUF == 3)
+            mainloop3((min(k0 + p.k_per_split, p.K) - k0) / BK);
+        else
+            mainloop((min(k0 + p.k_per_split, p.K) - k0) / BK, 0, false);
         epilogue(m0, n0, split);
     } else {
         // Persistent schedule over the grid's G workgroups: first R rounds of
