@@ -575,10 +575,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // MFMAs of a stage's last k-block left after the barrier (measured, same
     // box, alternating processes): the 256 x 256 8-wave tile runs 4096^3 in
     // 105.7 us with 24 of its 32 after the barrier against 112.3 with 8 (NN;
-    // NT 110.5 -> 104.5), while the 256 x 128 8-wave tile (16 per k-block)
-    // is 1-3% slower with more than 4 there; the fused q4 kernel keeps a
-    // quarter (its decode runs between the MFMAs before the barrier)
-    constexpr int TAIL = MS == 16 ? (!Q4 && NMF >= 32 ? NMF * 3 / 4 : NMF / 4)
+    // NT 110.5 -> 104.5); the 256 x 128 8-wave tile with three LDS stages
+    // runs best with all 16 after it (2048 x 4096 x 11008: 153.3 us with 4,
+    // 147.2 with 12, 145.2 with 16); the fused q4 kernel keeps a quarter (its
+    // decode runs between the MFMAs before the barrier)
+    constexpr int TAIL = MS == 16 ? (Q4 ? NMF / 4 : NBUF == 3 ? NMF : NMF >= 32 ? NMF * 3 / 4 : NMF / 4)
                                   : (NMF / 2 > 0 ? NMF / 2 : 1);
 
     // Main loop over the nk stages of the current tile, stage kt in buffer
