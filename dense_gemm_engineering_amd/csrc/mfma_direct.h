@@ -1,7 +1,8 @@
 // Direct-to-LDS macro-tile GEMM for fp16/bf16 on gfx950 (full tiles).
 //
 // BM x BN workgroup tile, WM x WN waves, 128-byte K stages in two LDS
-// buffers, accumulators in MS x MS MFMA blocks.
+// buffers (three for the 8-wave 256 x 128 tile), accumulators in MS x MS
+// MFMA blocks.
 //
 //  * Block size per wave count: one wave issuing independent 32x32x16 MFMAs
 //    back to back keeps its SIMD's matrix unit ~98% busy on gfx950, one
