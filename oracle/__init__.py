@@ -12,6 +12,10 @@ pages to pin it; it is pinned by its exact special cases (GELU(0) = 0, the
 odd symmetry of its tanh argument, the limits x and 0 for large |x|) and by
 an independent evaluation through the error function's relation
 (see ``tests/test_oracle_epilogue.py``).
+
+``dequant("q4_k", ...)`` is PARITY UNPINNED: the pages name the q4_K type but
+print no layout, so the super-block layout it decodes is a reading from
+outside them, and its golden blocks follow the same reading.
 """
 import ctypes
 import os

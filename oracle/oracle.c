@@ -57,9 +57,15 @@
  *  - Rounding.  binary64 -> binary16 / bfloat16 / binary32, round to nearest,
  *    ties to even, with gradual underflow and overflow to infinity.
  *
- * Every function here is pinned by the CPU test suite against brute force,
- * closed forms and library routines (numpy's float16 cast, exact rational
- * arithmetic); nothing here is checked only against itself.
+ * Every function here but one is pinned by the CPU test suite against brute
+ * force, closed forms and library routines (numpy's float16 cast, exact
+ * rational arithmetic).  The exception: oracle_dequant_q4_k is PARITY
+ * UNPINNED.  The pages name the q4_K type but print no layout, so its 6-bit
+ * scale/min packing and nibble order are a reading from outside them; its
+ * golden blocks and the test's packer follow that same reading, and no
+ * importable library decodes the format, so a wrong reading of the layout
+ * would pass every test.  Its arithmetic (two exact binary32 products, one
+ * binary32 difference, one binary16 rounding) is pinned; its layout is not.
  *
  * Built with -O2 -ffp-contract=off and no fast-math, so `acc += a*b` is a
  * rounded multiply followed by a rounded add, as written.

@@ -1,7 +1,7 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (automatic tile and split choice), on sampled output rows
-that the oracle computes one by one; the q4 dequant is compared in full,
-bit for bit.
+"""GPU parity of the q4 dequant (bit for bit: every scale pattern, every
+code, the full prefill weights, ragged, strided and unaligned layouts), the
+prefill page's tail shape, and the column-split schedule.  The full-size
+products are compared element by element in test_gpu_full_size.py.
 """
 import numpy as np
 import pytest
@@ -10,7 +10,7 @@ import torch
 import oracle
 import dense_gemm_engineering_amd.binding as dge
 from dense_gemm_engineering_amd import inputs
-from gpu_util import assert_bits, assert_close, bits_of, sample_rows, to_dev
+from gpu_util import assert_bits, assert_close, bits_of, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -18,42 +18,6 @@ pytestmark = pytest.mark.gpu
 def _ws(M, N, K, dtype=torch.float16):
     n = dge.gemm_workspace_size(M, N, K, dtype)
     return torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda") if n else None
-
-
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_square_4096_sampled_rows(dtype):
-    A, B = inputs.square4096(dtype)
-    dA, dB = to_dev(A, dtype), to_dev(B, dtype)
-    C = dge.gemm(dA, dB, out_dtype=torch.float16, workspace=_ws(4096, 4096, 4096))
-    torch.cuda.synchronize()
-    rows = sample_rows(4096, 48, seed=1)
-    T, U = oracle.gemm(A[rows], B, dtype)
-    assert_close(C[torch.from_numpy(rows).cuda()], T, U, what=dtype)
-
-
-def test_square_4096_integer_bit_exact_sampled_rows():
-    r = np.random.Generator(np.random.PCG64(2042))
-    A = inputs.to_bits(r.integers(-4, 5, (4096, 4096)).astype(float), "f16")
-    B = inputs.to_bits(r.integers(-4, 5, (4096, 4096)).astype(float), "f16")
-    for out in (torch.float32, torch.float16):
-        C = dge.gemm_f16(to_dev(A, "f16"), to_dev(B, "f16"), out_dtype=out)
-        torch.cuda.synchronize()
-        rows = sample_rows(4096, 24, seed=3)
-        T, _ = oracle.gemm(A[rows], B, "f16", want_U=False)
-        assert_bits(C[torch.from_numpy(rows).cuda()], T, what=str(out))
-
-
-@pytest.mark.parametrize("n", [1024, 2048, 4096])
-def test_fp32_ladder_sampled_rows(n):
-    A, B = inputs.fp32_square(n)
-    dA, dB = to_dev(A, "f32"), to_dev(B, "f32")
-    rows = sample_rows(n, 24, seed=n)
-    T, U = oracle.gemm(A[rows], B, "f32")
-    algos = ["naive", "lds_tiled", "mfma"] if n <= 2048 else ["mfma"]
-    for algo in algos:
-        C = dge.gemm_ex(dA, dB, out_dtype=torch.float32, algo=algo)
-        torch.cuda.synchronize()
-        assert_close(C[torch.from_numpy(rows).cuda()], T, U, what=algo)
 
 
 def test_dequant_every_scale_times_every_code():
@@ -128,21 +92,6 @@ def test_dequant_rejects_ragged_cols():
         dge.dequant_q4_f16(q, 4, 16)
 
 
-@pytest.mark.parametrize("shape", ["up", "attn", "down"])
-def test_prefill_full_size(shape):
-    A, q, N, K = inputs.prefill_projection(shape)
-    dA = to_dev(A, "f16")
-    w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
-    C = dge.prefill_q4_f16(dA, torch.from_numpy(q).cuda(), N, K, w16=w16,
-                           workspace=_ws(2048, N, K))
-    torch.cuda.synchronize()
-    W16 = oracle.dequant_q4(q, N, K)
-    assert np.array_equal(bits_of(w16), W16)
-    rows = sample_rows(2048, 16, seed=N + K)
-    T, U = oracle.gemm(A[rows], W16, "f16", trans_b=True)
-    assert_close(C[torch.from_numpy(rows).cuda()], T, U, what=shape)
-
-
 def test_prefill_tail_shape_unit_scales_exact():
     # the prefill page's tail shape (od = 70, nt = 33, id = 256); d = 1 makes
     # W16 the integers q - 8, so the product is exact
@@ -156,18 +105,6 @@ def test_prefill_tail_shape_unit_scales_exact():
     torch.cuda.synchronize()
     T, _, _ = oracle.prefill(A, q, N, K, want_U=False)
     assert_bits(C, T)
-
-
-@pytest.mark.parametrize("N", [160, 32])
-def test_tall_skinny_bias_gelu_sampled_rows(N):
-    X, W, bias = inputs.tall_skinny(N)
-    C = dge.gemm_f16(to_dev(X, "f16"), to_dev(W, "f16"), out_dtype=torch.float16,
-                     epi="bias_gelu", bias=to_dev(bias, "f16"))
-    torch.cuda.synchronize()
-    rows = sample_rows(65536, 256, seed=N)
-    b = oracle.decode(bias, "f16")
-    T, U = oracle.gemm(X[rows], W, "f16", epi="bias_gelu", bias=b)
-    assert_close(C[torch.from_numpy(rows).cuda()], T, U, bias=b, what="N=%d" % N)
 
 
 @pytest.mark.parametrize("trans_b", [False, True])
