@@ -14,7 +14,9 @@ LIB_PATH = os.path.join(_HERE, "libdge_gemm.so")
 
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_NOT_SUPPORTED",
-                3: "GEMM_ERR_WORKSPACE", 4: "GEMM_ERR_LAUNCH", 5: "GEMM_ERR_DEVICE"}
+                3: "GEMM_ERR_WORKSPACE", 4: "GEMM_ERR_LAUNCH", 5: "GEMM_ERR_DEVICE",
+                6: "GEMM_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20
 EPI = {"none": 0, "bias": 1, "bias_gelu": 2}
 OUT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 IN = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2}
@@ -24,7 +26,8 @@ TILE = {"auto": 0, "256x256": 1, "256x128": 2, "128x128": 3, "128x64": 4, "256x2
 QTYPE = {"q4_0": 0, "q4_k": 1, "q6_k": 2, "q6_k_224": 3}
 
 # Every symbol include/gemm.h declares.
-EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "dequant_q4_f16", "prefill_q4_f16",
+EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "gemm_ex_noalloc", "dequant_q4_f16",
+           "prefill_q4_f16",
            "gemm_q4_f16", "dequant_f16", "prefill_f16",
            "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_workspace_size_streamk",
            "gemm_status_string", "gemm_init")
@@ -61,6 +64,8 @@ def lib():
             fn.restype = i32
         L.gemm_ex.argtypes = [i32] + gemm_args[:-1] + [ctypes.POINTER(Tuning), vp]
         L.gemm_ex.restype = i32
+        L.gemm_ex_noalloc.argtypes = [i32] + gemm_args[:-3] + [ctypes.POINTER(Tuning), vp]
+        L.gemm_ex_noalloc.restype = i32
         L.dequant_q4_f16.argtypes = [vp, vp, i64, i64, i64, vp]
         L.dequant_q4_f16.restype = i32
         L.prefill_q4_f16.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, i64, i32, i32, vp, vp, sz,
@@ -136,7 +141,11 @@ def _gemm_call(fn_name, A, B, C, trans_b, alpha, beta, out_dtype, epi, bias, wor
             float(beta), _ptr(C), _ld(C, "C"), OUT[C.dtype], EPI[epi], _ptr(bias),
             _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()]
     L = lib()
-    if fn_name == "gemm_ex":
+    if fn_name == "gemm_ex_noalloc":
+        st = L.gemm_ex_noalloc(IN[A.dtype], *args[:-2],
+                               ctypes.byref(tuning) if tuning is not None else None,
+                               _stream(stream))
+    elif fn_name == "gemm_ex":
         st = L.gemm_ex(IN[A.dtype], *args, ctypes.byref(tuning) if tuning is not None else None,
                        _stream(stream))
     else:
@@ -172,6 +181,17 @@ def gemm_ex(A, B, C=None, *, trans_b=False, alpha=1.0, beta=0.0, out_dtype=None,
     t = Tuning(ALGO[algo], TILE[tile], int(splits))
     return _gemm_call("gemm_ex", A, B, C, trans_b, alpha, beta, out_dtype, epi, bias, workspace,
                       stream, tuning=t)
+
+
+def gemm_ex_noalloc(A, B, C=None, *, trans_b=False, alpha=1.0, beta=0.0, out_dtype=None,
+                    epi="none", bias=None, algo="auto", tile="auto", splits=0, stream=None):
+    """gemm_ex with the library's static scratch in place of a workspace (the
+    call allocates nothing; calls overlapping on one device race)."""
+    if out_dtype is None:
+        out_dtype = torch.float32 if A.dtype == torch.float32 else torch.float16
+    t = Tuning(ALGO[algo], TILE[tile], int(splits))
+    return _gemm_call("gemm_ex_noalloc", A, B, C, trans_b, alpha, beta, out_dtype, epi, bias,
+                      None, stream, tuning=t)
 
 
 def gemm(A, B, C=None, **kw):

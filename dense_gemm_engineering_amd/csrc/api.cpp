@@ -13,6 +13,13 @@
 
 #include "launch.h"
 
+// Scratch of gemm_ex_noalloc: its split-K partial sums and its stream-K
+// partial tiles and arrival counters live here instead of in a caller
+// workspace.  Each device holds one copy from the library's load until the
+// process ends.  In host code the name is only a handle: the device address
+// is looked up once per device at initialisation and kept per device.
+static __device__ __align__(256) unsigned char scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace dge;
@@ -20,8 +27,9 @@ using namespace dge;
 constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
-    int ok;       // 1 = gfx950, usable
-    int cus;      // compute units
+    int ok;         // 1 = gfx950, usable
+    int cus;        // compute units
+    void* scratch;  // this device's copy of `scratch` (null if it could not be resolved)
 };
 
 std::once_flag g_dev_once[kMaxDevices];
@@ -35,11 +43,14 @@ gemm_status_t current_device(DeviceInfo* out) {
     }
     std::call_once(g_dev_once[dev], [dev]() {
         hipDeviceProp_t prop;
-        DeviceInfo info{0, 0};
+        DeviceInfo info{0, 0, nullptr};
         if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
             std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && skinny_init() == hipSuccess) {
             info.ok = 1;
             info.cus = prop.multiProcessorCount;
+            // with `dev` current: its copy of the no-allocation scratch
+            void* sp = nullptr;
+            if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) == hipSuccess) info.scratch = sp;
         }
         (void)hipGetLastError();
         g_dev[dev] = info;
@@ -729,6 +740,26 @@ gemm_status_t gemm_ex(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float 
                     tuning);
 }
 
+gemm_status_t gemm_ex_noalloc(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float alpha,
+                              const void* A, int64_t lda, const void* B, int64_t ldb,
+                              int trans_b, float beta, void* C, int64_t ldc, gemm_out_t c_type,
+                              gemm_epilogue_t epi, const void* bias, const gemm_tuning_t* tuning,
+                              void* stream) {
+    Gemm g = make_gemm((int)in_type, M, N, K, alpha, A, lda, B, ldb, trans_b, beta, C, ldc,
+                       c_type, epi, bias, nullptr, 0, stream);
+    gemm_status_t st = validate(g);
+    if (st != GEMM_OK || g.M == 0 || g.N == 0) return st;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    if (!dev.scratch) return GEMM_ERR_DEVICE;
+    // the schedule is chosen as for a caller workspace of the scratch's size;
+    // a request that needs more (an explicit split or stream-K) is rejected
+    g.ws = dev.scratch;
+    g.ws_bytes = GEMM_NOALLOC_SCRATCH_BYTES;
+    st = run_gemm(g, tuning);
+    return st == GEMM_ERR_WORKSPACE ? GEMM_ERR_SCRATCH : st;
+}
+
 gemm_status_t dequant_q4_f16(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,
                              void* stream) {
     if (rows < 0 || cols < 0 || cols % 32 != 0 || ldo < cols) return GEMM_ERR_INVALID_VALUE;
@@ -905,6 +936,8 @@ const char* gemm_status_string(gemm_status_t s) {
         case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: workspace too small for the split";
         case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
         case GEMM_ERR_DEVICE: return "GEMM_ERR_DEVICE: no usable gfx950 device";
+        case GEMM_ERR_SCRATCH:
+            return "GEMM_ERR_SCRATCH: the request needs more than the 32 MiB static scratch";
         default: return "unknown gemm_status_t";
     }
 }

@@ -84,8 +84,13 @@ typedef enum {
     GEMM_ERR_NOT_SUPPORTED = 2, /* valid request the library does not implement */
     GEMM_ERR_WORKSPACE = 3,     /* explicit split request without enough workspace */
     GEMM_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
-    GEMM_ERR_DEVICE = 5         /* no usable gfx950 device is current */
+    GEMM_ERR_DEVICE = 5,        /* no usable gfx950 device is current */
+    GEMM_ERR_SCRATCH = 6        /* gemm_ex_noalloc: the request needs more scratch than
+                                   GEMM_NOALLOC_SCRATCH_BYTES */
 } gemm_status_t;
+
+/* Size of the static per-device scratch of gemm_ex_noalloc (32 MiB). */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum { GEMM_EPI_NONE = 0, GEMM_EPI_BIAS = 1, GEMM_EPI_BIAS_GELU = 2 } gemm_epilogue_t;
 
@@ -193,6 +198,27 @@ gemm_status_t gemm_ex(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float 
                       float beta, void* C, int64_t ldc, gemm_out_t c_type, gemm_epilogue_t epi,
                       const void* bias, void* workspace, size_t workspace_bytes,
                       const gemm_tuning_t* tuning, void* stream);
+
+/* gemm_ex without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split-K partial sums and the
+ * stream-K partial tiles and arrival counters go to a static scratch array
+ * of GEMM_NOALLOC_SCRATCH_BYTES that the library holds on each device from
+ * its load until the process ends; the call itself allocates nothing.  The
+ * schedule is the one gemm_ex picks with a workspace of that size; a request
+ * that needs more (an explicit split whose partials exceed it, or stream-K
+ * on a grid whose partial tiles exceed it) returns GEMM_ERR_SCRATCH and
+ * enqueues nothing.  The caller still passes A, B, C and bias, with the
+ * conventions above.  Every call on one device shares that device's
+ * scratch: calls that overlap in time on one device (concurrent streams, or
+ * host threads on different streams) race and give undefined results; calls
+ * ordered on one stream are safe (each clears the counters it needs and
+ * writes every partial it reads). */
+gemm_status_t gemm_ex_noalloc(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float alpha,
+                              const void* A, int64_t lda, const void* B, int64_t ldb,
+                              int trans_b, float beta, void* C, int64_t ldc, gemm_out_t c_type,
+                              gemm_epilogue_t epi, const void* bias, const gemm_tuning_t* tuning,
+                              void* stream);
 
 /* q4 -> binary16.  q holds rows * (cols/32) blocks of 18 bytes, row-major
  * (block (r, b) at byte 18 * (r * cols/32 + b)): a little-endian binary16

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert dge.gemm_status_string(s).startswith(dge.STATUS_NAMES[s])
     assert "unknown" in dge.gemm_status_string(99)
 
