@@ -74,40 +74,77 @@ def prefill_stack_tokens_per_s(t_attn, t_up, t_down, tokens=2048, layers=32):
 
 
 # ------------------------------------------------------------ timing
+#
+# Protocol: every figure is the median of several windows of back-to-back
+# launches, each window bracketed by HIP events on the launch stream (GPU
+# time) and by host synchronisation (wall time); before its first window a
+# leg runs back to back for a while without host syncs (the engine clock
+# needs a few hundred ms of load to settle).  The headline legs run
+# interleaved in a shuffled order, three times over, so that slow drift of
+# the clock or the box affects every leg alike.
 
-def time_launches(fn, steps, warmup, torch, warm_seconds=0.3):
-    """Run fn warmup times and then for at least warm_seconds (the engine
-    clock needs a few hundred ms of load to settle), then time `steps`
-    back-to-back calls between one pair of HIP events on torch's current
-    stream (the stream the binding launches on).  Returns (average GPU time
-    per call in s, host wall time of the synchronised bracket in s)."""
+MIN_TIMED_S = 0.05  # timed work per leg and repeat (windows are added to reach it)
+
+
+def _prewarm(fn, torch, seconds, est_s):
+    n = max(1, int(seconds / max(est_s, 1e-6)))
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+
+
+def time_windows(fn, steps, windows, torch, min_timed_s=MIN_TIMED_S):
+    """`windows` (or more, to reach min_timed_s) windows of `steps`
+    back-to-back calls.  Returns a list of (GPU seconds, wall seconds) per
+    window (per window, not per call)."""
+    out = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    total = 0.0
+    while len(out) < windows or total < min_timed_s:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu = e0.elapsed_time(e1) * 1e-3
+        out.append((gpu, wall))
+        total += gpu
+        if len(out) >= 1000:
+            break
+    return out
+
+
+def summarize(wins, steps):
+    """Per-call figures of a list of (gpu, wall) windows."""
+    g = np.array([w[0] for w in wins]) / steps
+    h = np.array([w[1] for w in wins]) / steps
+    med = float(np.median(g))
+    return {"us": med * 1e6, "us_min": float(g.min()) * 1e6, "us_max": float(g.max()) * 1e6,
+            "spread_pct": float((g.max() - g.min()) / med * 100.0), "windows": len(wins),
+            "steps_per_window": steps, "wall_us": float(np.median(h)) * 1e6}
+
+
+def time_leg(fn, steps, torch, windows=5, warm_seconds=0.3, warmup=3):
+    """Warm-up calls, a settling period, then the median of the windows."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    t_end = time.perf_counter() + warm_seconds
-    while time.perf_counter() < t_end:
-        for _ in range(20):
-            fn()
-        torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
+    fn()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) * 1e-3 / steps, wall
+    _prewarm(fn, torch, warm_seconds, time.perf_counter() - t0)
+    return summarize(time_windows(fn, steps, windows, torch), steps)
 
 
-def time_graph(fn, steps, torch, warm_seconds=0.3, reps=5):
-    """GPU time per call of fn for kernels too short for host launches to
-    keep the GPU busy: `steps` calls captured in one HIP graph (on torch's
-    capture stream, which the binding launches on), replayed after
-    warm_seconds of replays, reps replays between one pair of events.
-    Returns the average time per call in s."""
+def time_graph(fn, steps, torch, warm_seconds=0.3, windows=5):
+    """Per-call figures of kernels too short for host launches to keep the
+    GPU busy: `steps` calls captured in one HIP graph (on torch's capture
+    stream, which the binding launches on), replayed back to back for
+    warm_seconds, then one replay per window."""
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -117,18 +154,12 @@ def time_graph(fn, steps, torch, warm_seconds=0.3, reps=5):
     torch.cuda.synchronize()
     t_end = time.perf_counter() + warm_seconds
     while time.perf_counter() < t_end:
-        g.replay()
+        for _ in range(4):
+            g.replay()
         torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / (reps * steps)
+    res = summarize(time_windows(g.replay, 1, windows, torch), steps)
     del g
-    return t
+    return res
 
 
 def _strip_comments(src):
@@ -156,14 +187,19 @@ def _strip_comments(src):
     return "\n".join(l for l in lines if l)
 
 
-def _src_hash():
-    """Hash of the kernel and library sources, comments left out."""
+# the files that define the headline kernel (a committed traffic summary is
+# only used while they are unchanged)
+HEADLINE_KERNEL_FILES = ("device_common.h", "mfma_gemm.h", "mfma_direct.h", "mfma_instances.inc",
+                         "kernels_direct_f16.hip")
+
+
+def _src_hash(files=HEADLINE_KERNEL_FILES):
+    """Hash of the kernel sources, comments left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_engineering_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip", ".cpp", ".inc")):
-            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
-                h.update(f.encode() + _strip_comments(fh.read()).encode())
+    for f in sorted(files):
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -197,11 +233,90 @@ def _dev(bits, dtype, torch):
     return torch.from_numpy(bits.view(np.int16).copy()).view(tdt).cuda()
 
 
-def _med(x):
-    return float(np.median(x))
+def clock_of(clk):
+    """Engine clock from per-workgroup records (shader-clock and 100 MHz
+    real-time counters at start and end): the mean over workgroups of
+    shader cycles / real time, in MHz, and the launch's span in us."""
+    c = clk.view(-1, 4).cpu().numpy().astype(np.float64)
+    c = c[c[:, 3] > c[:, 1]]
+    if len(c) == 0:
+        return None, None
+    mhz = float(np.mean((c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1]) * 100.0))
+    span_us = float((c[:, 3].max() - c[:, 1].min()) / 100.0)
+    return mhz, span_us
 
 
-def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
+def bench_headline(dge, inputs, torch, steps, windows, repeats, warmup, dtype, seed=0):
+    """The 4096^3 legs, interleaved: the headline GEMM (fp16 out), the same
+    product with fp32 output, the bf16-operand product, the GEMM with clock
+    records, and the MFMA-only probe on the same operands.  Returns per-leg
+    window lists and the clock records."""
+    M = N = K = 4096
+    A, B = inputs.square4096(dtype)
+    dA, dB = _dev(A, dtype, torch), _dev(B, dtype, torch)
+    Ab, Bb = inputs.square4096("bf16")
+    dAb, dBb = _dev(Ab, "bf16", torch), _dev(Bb, "bf16", torch)
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    wsz = dge.gemm_workspace_size(M, N, K, dA.dtype)
+    work = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda") if wsz else None
+    gemm = dge.gemm_f16 if dtype == "f16" else dge.gemm_bf16
+    clk = torch.zeros(4 * 1024, dtype=torch.int64, device="cuda")
+    clk_mfma = torch.zeros(4 * dge.PROBE_MFMA_GRID, dtype=torch.int64, device="cuda")
+    probe_out = torch.empty(dge.PROBE_MFMA_GRID * 512, dtype=torch.float32, device="cuda")
+    # the MFMA probe reads B as rows (the N x K view): a transposed copy of B
+    dBt = dB.t().contiguous()
+    legs = {
+        "gemm": lambda: gemm(dA, dB, C, workspace=work),
+        "gemm_f32out": lambda: gemm(dA, dB, C32, workspace=work),
+        "bf16": lambda: dge.gemm_bf16(dAb, dBb, C, workspace=work),
+        "gemm_clock": lambda: dge.probe_clock(dA, dB, C, clk),
+        "mfma_only": lambda: dge.probe_mfma(dA, dBt, 128, probe_out, clk_mfma),
+    }
+    for fn in legs.values():
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    wins = {k: [] for k in legs}
+    clocks = {"gemm_clock": [], "mfma_only": []}
+    names = list(legs)
+    for _ in range(repeats):
+        for k in [names[i] for i in rng.permutation(len(names))]:
+            fn = legs[k]
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            _prewarm(fn, torch, 0.2, time.perf_counter() - t0)
+            w = time_windows(fn, steps, windows, torch)
+            wins[k] += w
+            if k in clocks:
+                clocks[k].append(clock_of(clk if k == "gemm_clock" else clk_mfma))
+    del dA, dB, dAb, dBb, C, C32, work, dBt
+    return wins, clocks, A, B
+
+
+def bench_stream_peaks(dge, torch, windows=5, nbytes=1 << 30, grids=(2048, 4096, 8192, 16384, 32768)):
+    """Measured HBM ceilings: the best streaming read of 1 GiB and the best
+    copy of 1 GiB (2 GiB moved) over a few grid sizes, both well beyond the
+    256 MB Infinity Cache."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    read, copy = {}, {}
+    for g in grids:
+        r = time_leg(lambda: dge.probe_read(src, out, g), 1, torch, windows=windows,
+                     warm_seconds=0.1)
+        c = time_leg(lambda: dge.probe_copy(src, dst, g), 1, torch, windows=windows,
+                     warm_seconds=0.1)
+        read[g] = nbytes / (r["us"] * 1e-6) / 1e9
+        copy[g] = 2 * nbytes / (c["us"] * 1e-6) / 1e9
+    del src, dst
+    return {"read_GBs": max(read.values()), "copy_GBs": max(copy.values()),
+            "read_GBs_by_grid": read, "copy_GBs_by_grid": copy, "bytes": nbytes}
+
+
+def bench_prefill(dge, inputs, torch, steps, peaks, rotate_bytes=300e6):
     """Per shape: dequant (HBM-cold by rotating weight sets), GEMM, the fused
     q4 GEMM (gemm_q4_f16), tok/s."""
     out = {}
@@ -229,19 +344,22 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
             it[0] += 1
             dge.gemm_q4_f16(dA, qs[i], N, K, C, workspace=work)
 
-        td_eager, _ = time_launches(deq, steps, 3, torch)
         td = time_graph(deq, max(steps, nset), torch)
-        tg, _ = time_launches(gem, steps, 3, torch)
-        tf, _ = time_launches(fused, steps, 3, torch)
-        out[shape] = {"N": N, "K": K, "dequant_us": td * 1e6, "dequant_us_eager": td_eager * 1e6,
-                      "gemm_us": tg * 1e6,
-                      "dequant_GBs": dequant_alg_bytes(N, K) / td / 1e9,
-                      "dequant_hbm_frac": dequant_alg_bytes(N, K) / td / 1e9 / HBM_PEAK_GBS,
-                      "gemm_TFLOPs": gemm_flops(2048, N, K) / tg / 1e12,
-                      "gemm_mfma_frac": gemm_flops(2048, N, K) / tg / 1e12 / PEAK["f16"],
-                      "tok_s_dequant_per_call": 2048 / (td + tg),
-                      "tok_s_gemm_only": 2048 / tg,
-                      "fused_us": tf * 1e6, "tok_s_fused": 2048 / tf}
+        tg = time_leg(gem, steps, torch)
+        tf = time_leg(fused, steps, torch)
+        dq_gbs = dequant_alg_bytes(N, K) / (td["us"] * 1e-6) / 1e9
+        fl = gemm_flops(2048, N, K)
+        out[shape] = {"N": N, "K": K, "dequant_us": td["us"], "gemm_us": tg["us"],
+                      "fused_us": tf["us"], "dequant_timing": td, "gemm_timing": tg,
+                      "fused_timing": tf,
+                      "dequant_GBs": dq_gbs, "dequant_hbm_frac": dq_gbs / HBM_PEAK_GBS,
+                      "dequant_frac_of_measured_copy": dq_gbs / peaks["copy_GBs"],
+                      "gemm_TFLOPs": fl / tg["us"] / 1e6,
+                      "gemm_mfma_frac": fl / tg["us"] / 1e6 / PEAK["f16"],
+                      "fused_TFLOPs": fl / tf["us"] / 1e6,
+                      "tok_s_dequant_per_call": 2048 / ((td["us"] + tg["us"]) * 1e-6),
+                      "tok_s_gemm_only": 2048 / (tg["us"] * 1e-6),
+                      "tok_s_fused": 2048 / (tf["us"] * 1e-6)}
         del qs, ws, C, work, dA
     t = {k: (out[k]["dequant_us"] + out[k]["gemm_us"]) * 1e-6 for k in out}
     g = {k: out[k]["gemm_us"] * 1e-6 for k in out}
@@ -253,7 +371,7 @@ def bench_prefill(dge, inputs, torch, steps, rotate_bytes=300e6):
     return out
 
 
-def bench_kquant(dge, inputs, torch, steps, prefill, rotate_bytes=300e6):
+def bench_kquant(dge, inputs, torch, steps, prefill, peaks, rotate_bytes=300e6):
     """The super-block formats: dequant_f16 per prefill shape (HBM-cold by
     rotating weight sets); two-pass tok/s with the fp16 GEMM time measured by
     the prefill leg (the GEMM is the same one)."""
@@ -273,22 +391,22 @@ def bench_kquant(dge, inputs, torch, steps, prefill, rotate_bytes=300e6):
                 it[0] += 1
                 dge.dequant_f16(qtype, qs[i], N, K, out=ws[i])
 
-            td_eager, _ = time_launches(deq, steps, 3, torch)
             td = time_graph(deq, max(steps, nset), torch)
-            tg = prefill[shape]["gemm_us"] * 1e-6
-            res[shape] = {"dequant_us": td * 1e6, "dequant_us_eager": td_eager * 1e6,
-                          "dequant_GBs": alg / td / 1e9,
-                          "dequant_hbm_frac": alg / td / 1e9 / HBM_PEAK_GBS,
-                          "tok_s_dequant_per_call": 2048 / (td + tg)}
+            gbs = alg / (td["us"] * 1e-6) / 1e9
+            tg = prefill[shape]["gemm_us"]
+            res[shape] = {"dequant_us": td["us"], "dequant_timing": td, "dequant_GBs": gbs,
+                          "dequant_hbm_frac": gbs / HBM_PEAK_GBS,
+                          "dequant_frac_of_measured_copy": gbs / peaks["copy_GBs"],
+                          "tok_s_dequant_per_call": 2048 / ((td["us"] + tg) * 1e-6)}
             del qs, ws
-        t = {k: res[k]["dequant_us"] * 1e-6 + prefill[k]["gemm_us"] * 1e-6 for k in res}
+        t = {k: (res[k]["dequant_us"] + prefill[k]["gemm_us"]) * 1e-6 for k in res}
         res["stack_7b_like"] = {
             "tok_s_dequant_per_call": prefill_stack_tokens_per_s(t["attn"], t["up"], t["down"])}
         out[qtype] = res
     return out
 
 
-def bench_streamk(dge, inputs, torch, steps):
+def bench_streamk(dge, torch, steps):
     """The persistent schedule with a stream-K tail (algo "streamk", tile
     chosen by its model) beside the default schedule, fp16 N x K weights."""
     out = {}
@@ -301,18 +419,18 @@ def bench_streamk(dge, inputs, torch, steps):
         n = max(dge.gemm_workspace_size(M, N, K, torch.float16),
                 dge.gemm_workspace_size_streamk(M, N, K))
         ws = torch.empty(n // 4 + 1, dtype=torch.float32, device="cuda")
-        td, _ = time_launches(lambda: dge.gemm_f16(A, B, C, trans_b=True, workspace=ws), steps, 3,
-                              torch)
-        ts, _ = time_launches(lambda: dge.gemm_ex(A, B, C, trans_b=True, workspace=ws,
-                                                  algo="streamk"), steps, 3, torch)
-        out[name] = {"default_us": td * 1e6, "streamk_us": ts * 1e6,
-                     "default_TFLOPs": gemm_flops(M, N, K) / td / 1e12,
-                     "streamk_TFLOPs": gemm_flops(M, N, K) / ts / 1e12}
+        td = time_leg(lambda: dge.gemm_f16(A, B, C, trans_b=True, workspace=ws), steps, torch)
+        ts = time_leg(lambda: dge.gemm_ex(A, B, C, trans_b=True, workspace=ws, algo="streamk"),
+                      steps, torch)
+        fl = gemm_flops(M, N, K)
+        out[name] = {"default_us": td["us"], "streamk_us": ts["us"],
+                     "default_TFLOPs": fl / td["us"] / 1e6, "streamk_TFLOPs": fl / ts["us"] / 1e6,
+                     "default_timing": td, "streamk_timing": ts}
         del A, B, C, ws
     return out
 
 
-def bench_decode(dge, inputs, torch, steps, rotate_bytes=300e6):
+def bench_decode(dge, inputs, torch, steps, peaks, rotate_bytes=300e6):
     """The decode shape: M input rows against one 4096 x 4096 fp16 weight
     (HBM-cold by rotating weight copies); bound by reading W once."""
     out = {}
@@ -331,16 +449,18 @@ def bench_decode(dge, inputs, torch, steps, rotate_bytes=300e6):
             it[0] += 1
             dge.gemm_f16(dX, Ws[i], C, trans_b=True)
 
-        t_eager, _ = time_launches(run, steps, 3, torch)
         t = time_graph(run, max(steps, nset), torch)
         alg = gemm_alg_bytes(M, N, K, 2, 2)
-        out["M%d" % M] = {"us": t * 1e6, "us_eager": t_eager * 1e6, "GBs": alg / t / 1e9,
-                          "hbm_frac": alg / t / 1e9 / HBM_PEAK_GBS, "tokens_per_s": M / t}
+        gbs = alg / (t["us"] * 1e-6) / 1e9
+        out["M%d" % M] = {"us": t["us"], "timing": t, "GBs": gbs,
+                          "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "frac_of_measured_read": gbs / peaks["read_GBs"],
+                          "tokens_per_s": M / (t["us"] * 1e-6)}
     del Ws
     return out
 
 
-def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
+def bench_skinny(dge, inputs, torch, steps, peaks, rotate_bytes=300e6):
     out = {}
     for N in (160, 32):
         X, W, bias = inputs.tall_skinny(N)
@@ -356,29 +476,18 @@ def bench_skinny(dge, inputs, torch, steps, rotate_bytes=300e6):
             it[0] += 1
             dge.gemm_f16(Xs[i], dW, Cs[i], epi="bias_gelu", bias=db)
 
-        t_eager, _ = time_launches(run, steps, 3, torch)
         t = time_graph(run, max(steps, nset), torch)
         # the same call on one input set: its 25-42 MB stay in the Infinity Cache
         t_warm = time_graph(lambda: dge.gemm_f16(Xs[0], dW, Cs[0], epi="bias_gelu", bias=db),
                             steps, torch)
-        out["N%d" % N] = {"us": t * 1e6, "us_eager": t_eager * 1e6, "GBs": alg / t / 1e9,
-                          "hbm_frac": alg / t / 1e9 / HBM_PEAK_GBS,
-                          "TFLOPs": gemm_flops(65536, N, 160) / t / 1e12,
-                          "us_cache_warm": t_warm * 1e6}
+        gbs = alg / (t["us"] * 1e-6) / 1e9
+        out["N%d" % N] = {"us": t["us"], "timing": t, "GBs": gbs,
+                          "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "frac_of_measured_copy": gbs / peaks["copy_GBs"],
+                          "TFLOPs": gemm_flops(65536, N, 160) / (t["us"] * 1e-6) / 1e12,
+                          "us_cache_warm": t_warm["us"]}
         del Xs, Cs
     return out
-
-
-def bench_bf16_square(dge, inputs, torch, steps):
-    """The 4096^3 workload with bf16 operands (N(0,1)/sqrt(K)), fp16 output."""
-    A, B = inputs.square4096("bf16")
-    dA, dB = _dev(A, "bf16", torch), _dev(B, "bf16", torch)
-    C = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
-    n = dge.gemm_workspace_size(4096, 4096, 4096, torch.bfloat16)
-    ws = torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda") if n else None
-    t, _ = time_launches(lambda: dge.gemm_bf16(dA, dB, C, workspace=ws), steps, 3, torch)
-    tf = gemm_flops(4096, 4096, 4096) / t / 1e12
-    return {"us": t * 1e6, "TFLOPs": tf, "mfma_frac": tf / PEAK["bf16"]}
 
 
 def bench_ladder(dge, inputs, torch, steps):
@@ -391,17 +500,28 @@ def bench_ladder(dge, inputs, torch, steps):
         algos = ["naive", "lds_tiled", "mfma"] if n <= 2048 else ["lds_tiled", "mfma"]
         for algo in algos:
             s = max(2, steps // 10) if algo != "mfma" else steps
-            t, _ = time_launches(lambda: dge.gemm_ex(dA, dB, C, algo=algo), s, 1, torch,
-                                 warm_seconds=0.1)
-            row[algo] = {"us": t * 1e6, "TFLOPs": gemm_flops(n, n, n) / t / 1e12,
-                         "fp32_mfma_frac": gemm_flops(n, n, n) / t / 1e12 / PEAK["f32"]}
+            t = time_leg(lambda: dge.gemm_ex(dA, dB, C, algo=algo), s, torch, warm_seconds=0.1)
+            tf = gemm_flops(n, n, n) / (t["us"] * 1e-6) / 1e12
+            row[algo] = {"us": t["us"], "TFLOPs": tf, "fp32_mfma_frac": tf / PEAK["f32"],
+                         "timing": t}
         out["n%d" % n] = row
     return out
 
 
-def cpu_baseline(A, B, seconds_target=15.0):
-    """The oracle, untuned, on all host cores: the first rows of the 4096^3
-    product (all of them when that takes at most about 2x seconds_target)."""
+# ------------------------------------------------------------ CPU oracle
+
+def _oracle_rate(fn, flops, threads):
+    t0 = time.perf_counter()
+    fn(threads)
+    t = time.perf_counter() - t0
+    return {"seconds": t, "GFLOPs": flops / t / 1e9, "threads": threads}
+
+
+def cpu_baseline(A, B, inputs, seconds_target=15.0):
+    """The oracle, untuned (binary64 i-k-j loops), on the host cores: the
+    headline figure on the first rows of the 4096^3 product (all of them when
+    that takes at most about 2x seconds_target), and per workload a bounded
+    sample on all cores, plus one thread for the 256^3 and 1024^3 products."""
     import oracle
     cores = oracle.default_threads()
     probe = max(cores, 64)
@@ -414,31 +534,69 @@ def cpu_baseline(A, B, seconds_target=15.0):
     t0 = time.perf_counter()
     oracle.gemm(A[:rows], B, "f16", want_U=False, threads=cores)
     t = time.perf_counter() - t0
-    return {"value": gemm_flops(rows, 4096, 4096) / t / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "seconds": t,
-            "sample": "rows 0..%d of the 4096^3 fp16 product (%.1f GFLOP), binary64 "
-                      "accumulation, row-parallel over %d threads"
-                      % (rows - 1, gemm_flops(rows, 4096, 4096) / 1e9, cores)}
+    res = {"value": gemm_flops(rows, 4096, 4096) / t / 1e12, "unit": "TFLOP/s", "cores": cores,
+           "kind": "oracle", "seconds": t,
+           "sample": "rows 0..%d of the 4096^3 fp16 product (%.1f GFLOP), binary64 "
+                     "accumulation, row-parallel over %d threads"
+                     % (rows - 1, gemm_flops(rows, 4096, 4096) / 1e9, cores)}
+    per = {}
+    a1, b1 = inputs.square256()
+    for th in (cores, 1):
+        per["square256_threads%d" % th] = _oracle_rate(
+            lambda t: oracle.gemm(a1, b1, "f16", want_U=False, threads=t), gemm_flops(256, 256, 256), th)
+    a3, b3 = inputs.fp32_square(1024)
+    for th in (cores, 1):
+        per["fp32_1024_threads%d" % th] = _oracle_rate(
+            lambda t: oracle.gemm(a3, b3, "f32", want_U=False, threads=t), gemm_flops(1024, 1024, 1024), th)
+    for n in (2048, 4096):
+        a, b = inputs.fp32_square(n)
+        r = 256
+        per["fp32_%d_rows%d" % (n, r)] = _oracle_rate(
+            lambda t: oracle.gemm(a[:r], b, "f32", want_U=False, threads=t), gemm_flops(r, n, n), cores)
+    for shape in ("up", "attn", "down"):
+        a, q, N, K = inputs.prefill_projection(shape)
+        r = 64
+        W16 = oracle.dequant_q4(q, N, K)
+        per["prefill_%s_rows%d" % (shape, r)] = _oracle_rate(
+            lambda t: oracle.gemm(a[:r], W16, "f16", trans_b=True, want_U=False, threads=t),
+            gemm_flops(r, N, K), cores)
+        t0 = time.perf_counter()
+        oracle.dequant_q4(q, N, K)
+        dt = time.perf_counter() - t0
+        per["dequant_%s" % shape] = {"seconds": dt, "threads": 1,
+                                     "GBs": dequant_alg_bytes(N, K) / dt / 1e9}
+    for N in (160, 32):
+        x, w, bias = inputs.tall_skinny(N)
+        bd = oracle.decode(bias, "f16")
+        per["skinny_N%d" % N] = _oracle_rate(
+            lambda t: oracle.gemm(x, w, "f16", epi="bias_gelu", bias=bd, want_U=False, threads=t),
+            gemm_flops(65536, N, 160), cores)
+    res["per_workload"] = per
+    return res
 
+
+# ------------------------------------------------------------ main
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 500 back-to-back launches (~55 ms): 50-launch windows of the same kernel
-    # in one process spread over +-2% on this part; 500-launch ones agree to 0.3%
-    ap.add_argument("--steps", type=int, default=500)
+    # launches per timed window (each leg: the median of at least --windows
+    # windows, more when they add up to under 50 ms)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--windows", type=int, default=7)
+    ap.add_argument("--repeats", type=int, default=3)
     ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="only the headline GEMM")
+    ap.add_argument("--no-extra", action="store_true", help="only the 4096^3 legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only a plain 256 MiB device-to-device copy, 5 times (the reference "
                          "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: every GPU box here has one, and the library has "
+              "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -458,20 +616,26 @@ def main():
 
     dge.gemm_init()
     M = N = K = 4096
-    A, B = inputs.square4096(args.dtype)
-    dA, dB = _dev(A, args.dtype, torch), _dev(B, args.dtype, torch)
-    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    wsz = dge.gemm_workspace_size(M, N, K, dA.dtype)
-    work = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda") if wsz else None
-    fn = (lambda: dge.gemm_f16(dA, dB, C, workspace=work)) if args.dtype == "f16" else \
-        (lambda: dge.gemm_bf16(dA, dB, C, workspace=work))
-
-    avg_kernel, wall = time_launches(fn, args.steps, args.warmup, torch)
     flops = gemm_flops(M, N, K)
-    ms_per_step = wall / args.steps * 1e3
-    value = flops * args.steps / wall / 1e12
-    achieved = flops / avg_kernel / 1e12
+    wins, clocks, A, B = bench_headline(dge, inputs, torch, args.steps, args.windows,
+                                        args.repeats, args.warmup, args.dtype)
+    head = summarize(wins["gemm"], args.steps)
+    ms_per_step = head["wall_us"] * 1e-3
+    value = flops / (head["wall_us"] * 1e-6) / 1e12
+    achieved = flops / (head["us"] * 1e-6) / 1e12
+    legs = {k: summarize(w, args.steps) for k, w in wins.items()}
+    mfma_only = flops / (legs["mfma_only"]["us"] * 1e-6) / 1e12
+
+    def med_clock(k):
+        v = [c[0] for c in clocks[k] if c[0]]
+        return float(np.median(v)) if v else None
+
+    sclk = med_clock("gemm_clock")
+    sclk_mfma = med_clock("mfma_only")
+    spans = [c[1] for c in clocks["gemm_clock"] if c[1]]
+    peaks = bench_stream_peaks(dge, torch)
     traffic = _traffic("gemm_%s_4096" % args.dtype)
+    peak = PEAK[args.dtype]
     line = {
         "metric": "TFLOP/s fp16 GEMM 4096^3 (% of MFMA peak); 2K-token prefill GEMM tok/s",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -481,26 +645,47 @@ def main():
                                "N(0,1)/sqrt(K), fp32 accumulate, fp16 output, alpha=1, beta=0"
                                % args.dtype, "M": M, "N": N, "K": K, "accumulate": "f32",
                    "output": "f16", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK[args.dtype],
-                     "unit": "TFLOP/s", "frac": achieved / PEAK[args.dtype],
-                     "traffic": traffic,
-                     "kernel_us_mean": avg_kernel * 1e6,
-                     "alg_bytes": gemm_alg_bytes(M, N, K, 2, 2),
-                     "kernel": "gemm_direct_kernel<fp16, 256x256 tile, 8 waves, 16x16x32 MFMA, K x N B>"},
+        "roofline": {
+            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic,
+            "kernel_us_median": head["us"], "kernel_us_min": head["us_min"],
+            "kernel_us_max": head["us_max"], "windows": head["windows"],
+            "steps_per_window": args.steps, "repeats": args.repeats,
+            "alg_bytes": gemm_alg_bytes(M, N, K, 2, 2),
+            "kernel": "gemm_direct_kernel<%s, 256x256 tile, 8 waves, 16x16x32 MFMA, K x N B>"
+                      % args.dtype,
+            # the engine clock over the same kernel (its own clock records) and
+            # the measured ceilings at the workload's data
+            "sclk_mhz": sclk,
+            "frac_at_sclk": achieved / (peak * sclk / 2400.0) if sclk else None,
+            "clock_launch_span_us": float(np.median(spans)) if spans else None,
+            "measured_peak": {"mfma_only_TFLOPs": mfma_only, "mfma_only_sclk_mhz": sclk_mfma,
+                              "mfma_only_us": legs["mfma_only"]["us"],
+                              "frac_of_mfma_only": achieved / mfma_only,
+                              "hbm_read_GBs": peaks["read_GBs"],
+                              "hbm_copy_GBs": peaks["copy_GBs"]},
+        },
+        "legs_4096": {
+            "gemm_f16out": legs["gemm"],
+            "gemm_f32out": dict(legs["gemm_f32out"], TFLOPs=flops / legs["gemm_f32out"]["us"] / 1e6),
+            "bf16_f16out": dict(legs["bf16"], TFLOPs=flops / legs["bf16"]["us"] / 1e6,
+                                mfma_frac=flops / legs["bf16"]["us"] / 1e6 / PEAK["bf16"]),
+            "gemm_with_clock_records": legs["gemm_clock"],
+            "mfma_only_probe": legs["mfma_only"],
+        },
+        "hbm_peaks": peaks,
     }
     if not args.no_extra:
         extra_steps = max(10, min(args.steps, 30))
-        line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps)
+        line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps, peaks)
         line["prefill_kquant"] = bench_kquant(dge, inputs, torch, extra_steps,
-                                              line["prefill_2048"])
-        if args.dtype == "f16":
-            line["bf16_4096"] = bench_bf16_square(dge, inputs, torch, 200)
-        line["streamk_vs_default"] = bench_streamk(dge, inputs, torch, extra_steps)
-        line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps)
-        line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps)
+                                              line["prefill_2048"], peaks)
+        line["streamk_vs_default"] = bench_streamk(dge, torch, extra_steps)
+        line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps, peaks)
+        line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps, peaks)
         line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(A, B, inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -30,7 +30,10 @@ EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "gemm_ex_noalloc", "d
            "prefill_q4_f16",
            "gemm_q4_f16", "dequant_f16", "prefill_f16",
            "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_workspace_size_streamk",
-           "gemm_status_string", "gemm_init")
+           "gemm_status_string", "gemm_init",
+           # measurement probes (include/gemm_probe.h)
+           "gemm_probe_clock", "gemm_probe_mfma", "gemm_probe_read", "gemm_probe_copy")
+PROBE_MFMA_GRID = 256
 
 
 class GemmError(RuntimeError):
@@ -88,6 +91,14 @@ def lib():
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_init.argtypes = []
         L.gemm_init.restype = i32
+        L.gemm_probe_clock.argtypes = [i32] + gemm_args[:-3] + [vp, i64, vp]
+        L.gemm_probe_clock.restype = i32
+        L.gemm_probe_mfma.argtypes = [i32, vp, i64, vp, i64, i64, i64, i32, vp, vp, vp]
+        L.gemm_probe_mfma.restype = i32
+        L.gemm_probe_read.argtypes = [vp, sz, i32, vp, vp]
+        L.gemm_probe_read.restype = i32
+        L.gemm_probe_copy.argtypes = [vp, vp, sz, i32, vp]
+        L.gemm_probe_copy.restype = i32
         _lib = L
     return _lib
 
@@ -264,6 +275,39 @@ def gemm_q4_f16(A, q, N, K, C=None, *, out_dtype=torch.float16, epi="none", bias
                              OUT[C.dtype], EPI[epi], _ptr(bias), _ptr(workspace), ws_bytes,
                              ctypes.byref(t), _stream(stream)), "gemm_q4_f16")
     return C
+
+
+def probe_clock(A, B, C, clk, *, trans_b=False, stream=None):
+    """The automatic GEMM C = A @ B (one data-parallel launch) with clock
+    records: clk is a uint64 (int64) device tensor of 4 values per workgroup."""
+    M, N, K, C = _prepare(A, B, C, trans_b, C.dtype)
+    _check(lib().gemm_probe_clock(IN[A.dtype], M, N, K, 1.0, _ptr(A), _ld(A, "A"), _ptr(B),
+                                  _ld(B, "B"), int(bool(trans_b)), 0.0, _ptr(C), _ld(C, "C"),
+                                  OUT[C.dtype], 0, None, _ptr(clk), clk.numel() // 4,
+                                  _stream(stream)), "gemm_probe_clock")
+    return C
+
+
+def probe_mfma(A, B, k_blocks, out, clk=None, stream=None):
+    """MFMA-only probe over operand fragments of A and B (>= 4096 rows)."""
+    _check(lib().gemm_probe_mfma(IN[A.dtype], _ptr(A), _ld(A, "A"), _ptr(B), _ld(B, "B"),
+                                 min(A.shape[0], B.shape[0]), min(A.shape[1], B.shape[1]),
+                                 int(k_blocks), _ptr(out), _ptr(clk), _stream(stream)),
+           "gemm_probe_mfma")
+
+
+def probe_read(src, out, grid, stream=None):
+    """Streaming read of src on `grid` workgroups; out: >= grid x 256 int32."""
+    assert out.numel() >= grid * 256
+    _check(lib().gemm_probe_read(_ptr(src), src.numel() * src.element_size(), int(grid),
+                                 _ptr(out), _stream(stream)), "gemm_probe_read")
+
+
+def probe_copy(src, dst, grid, stream=None):
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    _check(lib().gemm_probe_copy(_ptr(src), _ptr(dst), n, int(grid), _stream(stream)),
+           "gemm_probe_copy")
 
 
 def gemm_workspace_size(M, N, K, dtype=torch.float16):

@@ -2,6 +2,7 @@
 // schedule selection, launches on the caller's stream.  Declarations and the
 // contract of every entry point are in include/gemm.h.
 #include "gemm.h"
+#include "gemm_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -102,6 +103,10 @@ struct Gemm {
     size_t ws_bytes;
     hipStream_t stream;
     int b_q4;  // B is an N x K weight as q4 blocks (18 bytes per 32 weights)
+    // measurement only (gemm_probe_clock): per-workgroup clock records, and
+    // how many workgroups they can hold
+    unsigned long long* clk;
+    int64_t clk_cap;
 };
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
@@ -440,6 +445,7 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
         ColumnSplit cs;
         if (all && choose_column_split(g.M, g.N, g.K, g.dt, cus, g.ws ? g.ws_bytes : 0, all,
                                        allowed2, &cs)) {
+            if (g.clk) return GEMM_ERR_NOT_SUPPORTED;  // clock records cover one launch
             gemm_status_t st = run_mfma(column_range(g, 0, cs.n1), cs.tile, 1, cus, direct, 0, false);
             if (st != GEMM_OK) return st;
             // the rest with its tile; its split is chosen again against the
@@ -486,7 +492,7 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
             splits = 1;
         }
     }
-    MfmaArgs a;
+    MfmaArgs a{};
     a.A = g.A;
     a.B = g.B;
     a.C = g.C;
@@ -532,6 +538,12 @@ gemm_status_t run_mfma(const Gemm& g, int tile, int splits, int cus, int direct,
     }
     const bool use_direct = direct && fast && g.dt != IN_F32 && direct_ld_ok(g) &&
                             (g.trans_b || ts.bn >= 128) && env_int("GEMM_DIRECT", 1) != 0;
+    if (g.clk) {
+        // clock records: one data-parallel launch of a direct-to-LDS kernel
+        if (g.b_q4 || !use_direct || sk || splits > 1 || nwg > g.clk_cap)
+            return GEMM_ERR_NOT_SUPPORTED;
+        a.clk = g.clk;
+    }
     if (sk && use_direct && aligned16(g.ws)) {
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n, S = g.K / bk;
         const int64_t G = sk_grid(tile, tiles * S, cus);
@@ -696,6 +708,8 @@ Gemm make_gemm(int dt, int64_t M, int64_t N, int64_t K, float alpha, const void*
     g.ws_bytes = workspace_bytes;
     g.stream = (hipStream_t)stream;
     g.b_q4 = 0;
+    g.clk = nullptr;
+    g.clk_cap = 0;
     return g;
 }
 
@@ -758,6 +772,66 @@ gemm_status_t gemm_ex_noalloc(gemm_in_t in_type, int64_t M, int64_t N, int64_t K
     g.ws_bytes = GEMM_NOALLOC_SCRATCH_BYTES;
     st = run_gemm(g, tuning);
     return st == GEMM_ERR_WORKSPACE ? GEMM_ERR_SCRATCH : st;
+}
+
+gemm_status_t gemm_probe_clock(gemm_in_t in_type, int64_t M, int64_t N, int64_t K, float alpha,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               int trans_b, float beta, void* C, int64_t ldc, gemm_out_t c_type,
+                               gemm_epilogue_t epi, const void* bias, unsigned long long* clk,
+                               int64_t clk_entries, void* stream) {
+    if (!clk || clk_entries <= 0 || ((uintptr_t)clk & 15)) return GEMM_ERR_INVALID_VALUE;
+    Gemm g = make_gemm((int)in_type, M, N, K, alpha, A, lda, B, ldb, trans_b, beta, C, ldc,
+                       c_type, epi, bias, nullptr, 0, stream);
+    g.clk = clk;
+    g.clk_cap = clk_entries;
+    gemm_status_t st = validate(g);
+    if (st != GEMM_OK || g.M == 0 || g.N == 0) return st;
+    if (g.K == 0 || g.dt == IN_F32) return GEMM_ERR_NOT_SUPPORTED;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    return run_mfma(g, GEMM_TILE_AUTO, 0, dev.cus, 1);
+}
+
+gemm_status_t gemm_probe_mfma(gemm_in_t in_type, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, int64_t rows, int64_t cols, int k_blocks, float* out,
+                              unsigned long long* clk, void* stream) {
+    if ((in_type != GEMM_IN_F16 && in_type != GEMM_IN_BF16) || !A || !B || !out ||
+        !aligned16(A) || !aligned16(B) || rows < 4096 || cols < 64 || lda < cols || ldb < cols ||
+        lda % 8 != 0 || ldb % 8 != 0 || lda > kMaxDim || ldb > kMaxDim || k_blocks < 1 ||
+        ((uintptr_t)clk & 15))
+        return GEMM_ERR_INVALID_VALUE;
+    DeviceInfo dev;
+    gemm_status_t st = current_device(&dev);
+    if (st != GEMM_OK) return st;
+    return launch_status(launch_probe_mfma((int)in_type, A, B, lda, ldb, k_blocks, out, clk,
+                                           (hipStream_t)stream));
+}
+
+gemm_status_t gemm_probe_read(const void* src, size_t bytes, int grid, unsigned* out,
+                              void* stream) {
+    if (!src || !out || !aligned16(src) || bytes % 16 != 0 || grid < 1 || grid > 65536)
+        return GEMM_ERR_INVALID_VALUE;
+    if (bytes == 0) return GEMM_OK;
+    DeviceInfo dev;
+    gemm_status_t st = current_device(&dev);
+    if (st != GEMM_OK) return st;
+    return launch_status(
+        launch_probe_read(src, (int64_t)(bytes / 16), out, grid, (hipStream_t)stream));
+}
+
+gemm_status_t gemm_probe_copy(const void* src, void* dst, size_t bytes, int grid, void* stream) {
+    if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes % 16 != 0 || grid < 1 ||
+        grid > 65536)
+        return GEMM_ERR_INVALID_VALUE;
+    if (bytes == 0) return GEMM_OK;
+    if (overlaps(Range{(uintptr_t)src, (uintptr_t)src + bytes},
+                 Range{(uintptr_t)dst, (uintptr_t)dst + bytes}))
+        return GEMM_ERR_INVALID_VALUE;
+    DeviceInfo dev;
+    gemm_status_t st = current_device(&dev);
+    if (st != GEMM_OK) return st;
+    return launch_status(
+        launch_probe_copy(src, dst, (int64_t)(bytes / 16), grid, (hipStream_t)stream));
 }
 
 gemm_status_t dequant_q4_f16(const void* q, void* out, int64_t rows, int64_t cols, int64_t ldo,

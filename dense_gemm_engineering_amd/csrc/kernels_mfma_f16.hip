@@ -1,9 +1,7 @@
-// MFMA macro-tile GEMM instances for f16 inputs.
+// Register-staged MFMA macro-tile GEMM instances for f16 inputs.
 #include "launch.h"
-#include "mfma_direct.h"
 
 #define DGE_DT IN_F16
+#define DGE_REGSTAGED 1
 #define DGE_LAUNCHER launch_mfma_f16
-#define DGE_DIRECT 1
-#define DGE_DIRECT_LAUNCHER launch_mfma_direct_f16
 #include "mfma_instances.inc"

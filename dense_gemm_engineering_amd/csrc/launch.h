@@ -78,4 +78,18 @@ hipError_t launch_dequant_q4(const void* q, void* out, int64_t rows, int64_t col
 hipError_t launch_dequant_kq(int qtype, const void* q, void* out, int64_t rows, int64_t cols,
                              int64_t ldo, int vec_out, hipStream_t s);
 
+// Measurement probes (kernels_probe.hip).  The MFMA probe runs
+// PROBE_MFMA_GRID workgroups of 8 waves over the 4096 x 4096 output of the
+// headline product (A and B need 4096 rows of at least 64 elements, 16-byte
+// aligned, leading dimensions a multiple of 8); out receives
+// PROBE_MFMA_GRID x 512 floats, clk (if set) 4 values per workgroup.  The
+// streaming probes take 16-byte chunks on `grid` workgroups of 256 threads;
+// out receives grid x 256 digests.
+constexpr int PROBE_MFMA_GRID = 256;
+hipError_t launch_probe_mfma(int dt, const void* A, const void* B, int64_t lda, int64_t ldb,
+                             int k_blocks, float* out, unsigned long long* clk, hipStream_t s);
+hipError_t launch_probe_read(const void* src, int64_t n16, unsigned* out, int grid,
+                             hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int grid, hipStream_t s);
+
 }  // namespace dge

@@ -720,6 +720,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
 
     if constexpr (!SK) {
         // one (tile, K slice) per workgroup
+        unsigned long long clk0 = 0, rt0 = 0;
+        if (p.clk) {
+            clk0 = __builtin_amdgcn_s_memtime();
+            rt0 = __builtin_amdgcn_s_memrealtime();
+        }
         const int ntiles = p.tiles_m * p.tiles_n;
         const int lin = remap_xcd(blockIdx.x, ntiles * p.splits);
         const int split = lin / ntiles;
@@ -733,6 +738,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         else
             mainloop((min(k0 + p.k_per_split, p.K) - k0) / BK, 0, false);
         epilogue(m0, n0, split);
+        if (p.clk) {
+            const unsigned long long clk1 = __builtin_amdgcn_s_memtime();
+            const unsigned long long rt1 = __builtin_amdgcn_s_memrealtime();
+            if (tid == 0) {
+                unsigned long long* c = p.clk + 4 * (int64_t)blockIdx.x;
+                c[0] = clk0;
+                c[1] = rt0;
+                c[2] = clk1;
+                c[3] = rt1;
+            }
+        }
     } else {
         // Persistent schedule over the grid's G workgroups: first R rounds of
         // whole tiles, round r giving tile r G + v to workgroup v (so the

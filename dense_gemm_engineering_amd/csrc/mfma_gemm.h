@@ -100,6 +100,10 @@ struct MfmaArgs {
     int sk_rounds;  // rounds of whole tiles before the stream-K tail
     float* sk_ws;
     unsigned* sk_cnt;
+    // measurement only (direct-to-LDS kernels, data-parallel schedule): when
+    // set, each workgroup records its shader-clock and 100 MHz real-time
+    // counters at its start and end, 4 values at clk + 4 blockIdx.x
+    unsigned long long* clk;
 };
 
 // Pack KPL elements loaded one by one (with a bound) into a 16-byte chunk.

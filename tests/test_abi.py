@@ -14,8 +14,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    with open(os.path.join(ROOT, "include", "gemm.h")) as f:
-        src = f.read()
+    src = ""
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            with open(os.path.join(ROOT, "include", h)) as f:
+                src += f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+([a-z_0-9]+)\s*\(", src,
                        flags=re.M)
