@@ -11,6 +11,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdge_gemm.so")
+# the diagnostic build of the same library (extra waits and barriers in the
+# direct-to-LDS kernels); only tests select it, through diag_library()
+LIB_DIAG_PATH = os.path.join(_HERE, "libdge_gemm_diag.so")
 
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_NOT_SUPPORTED",
@@ -46,17 +49,29 @@ class Tuning(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int), ("tile", ctypes.c_int), ("splits", ctypes.c_int)]
 
 
-_lib = None
+_libs = {}
+_active = [LIB_PATH]
+
+
+class diag_library:
+    """Context manager: calls inside it go to the diagnostic build."""
+
+    def __enter__(self):
+        _active.append(LIB_DIAG_PATH)
+        return self
+
+    def __exit__(self, *exc):
+        _active.pop()
+        return False
 
 
 def lib():
     """Load libdge_gemm.so (raises if it has not been built)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError("libdge_gemm.so is not built (run __graft_entry__.build()): %s"
-                              % LIB_PATH)
-        L = ctypes.CDLL(LIB_PATH)
+    path = _active[-1]
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise ImportError("%s is not built (run __graft_entry__.build())" % path)
+        L = ctypes.CDLL(path)
         i64, f32, vp, i32, sz = (ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
                                  ctypes.c_size_t)
         gemm_args = [i64, i64, i64, f32, vp, i64, vp, i64, i32, f32, vp, i64, i32, i32, vp, vp, sz,
@@ -99,8 +114,8 @@ def lib():
         L.gemm_probe_read.restype = i32
         L.gemm_probe_copy.argtypes = [vp, vp, sz, i32, vp]
         L.gemm_probe_copy.restype = i32
-        _lib = L
-    return _lib
+        _libs[path] = L
+    return _libs[path]
 
 
 def gemm_status_string(status):

@@ -13,6 +13,11 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdge_gemm.so")
+# the diagnostic build: the same library with every pipelined overlap of the
+# direct-to-LDS kernels removed by extra waits and barriers
+# (GEMM_DIAG_EXTRA_BARRIERS), whose bit-exact results the tests compare with
+# the normal build's
+LIB_DIAG = os.path.join(PKG, "libdge_gemm_diag.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["api.cpp", "kernels_mfma_f16.hip", "kernels_mfma_bf16.hip", "kernels_mfma_f32.hip",
@@ -28,9 +33,12 @@ CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, 
           "-packed-fp32-ops"]
 
 
-def _compile(src):
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+def _compile(job):
+    src, diag = job
+    obj = os.path.join(OBJDIR + ("_diag" if diag else ""), os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, "-x", "hip", "-c", os.path.join(HERE, src), "-o", obj] + CFLAGS
+    if diag:
+        cmd.append("-DGEMM_DIAG_EXTRA_BARRIERS=1")
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l and l.strip())
@@ -39,18 +47,28 @@ def _compile(src):
     return obj, errs
 
 
-def build(jobs=None, verbose=False):
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+
+
+def build(jobs=None, verbose=False, diag=True):
+    """Compile and link libdge_gemm.so (and, with diag, libdge_gemm_diag.so)."""
     os.makedirs(OBJDIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, len(os.sched_getaffinity(0))), 16)
+    os.makedirs(OBJDIR + "_diag", exist_ok=True)
+    work = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if diag else [])
+    jobs = jobs or min(len(work), max(1, len(os.sched_getaffinity(0))), 16)
     with ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(_compile, work))
     for _, errs in results:
         if errs and verbose:
             print(errs, file=sys.stderr)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    _link([o for o, _ in results[:n]], LIB)
+    if diag:
+        _link([o for o, _ in results[n:]], LIB_DIAG)
     return LIB
 
 

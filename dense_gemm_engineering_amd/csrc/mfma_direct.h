@@ -67,6 +67,26 @@
 
 namespace dge {
 
+// Diagnostic build (-DGEMM_DIAG_EXTRA_BARRIERS, libdge_gemm_diag.so): after
+// every group of direct loads, fragment reads, q4 decode writes and epilogue
+// staging writes, each wave waits for all its memory operations and meets
+// every other wave at a barrier.  Nothing then overlaps, so a missing wait
+// or barrier in the pipelined kernel (one wave's loads overwriting a buffer
+// another still reads) shows up as a difference between the two builds'
+// bit-exact results.  Every place it is used is reached by all waves of the
+// workgroup the same number of times.
+#if defined(GEMM_DIAG_EXTRA_BARRIERS)
+#define DGE_DIAG_SYNC()                     \
+    do {                                    \
+        __builtin_amdgcn_s_waitcnt(0);      \
+        __syncthreads();                    \
+    } while (0)
+#else
+#define DGE_DIAG_SYNC() \
+    do {                \
+    } while (0)
+#endif
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define DGE_LDS __attribute__((address_space(3)))
@@ -281,6 +301,7 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
                         *(DGE_LDS u32x2*)(stg + r * RB + (((cb >> 4) ^ (r & (CPR - 1))) << 4) + (cb & 15)) =
                             (u32x2){lo, hi};
                     }
+            DGE_DIAG_SYNC();
             // this wave's rows back as 16-byte pieces (the wave's own LDS
             // operations complete in order: no barrier)
 #pragma unroll
@@ -431,6 +452,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             if (IA + i < lo || IA + i >= hi) continue;
             lds_dma16_s(gb, b_off[i], lb + i * 1024);
         }
+        DGE_DIAG_SYNC();
     };
 
     // ---- q4 B producer: task t = (tile row t / 2, block t % 2 of the stage)
@@ -478,6 +500,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
                     (u32x4){o[0], o[1], o[2], o[3]};
             }
         }
+        DGE_DIAG_SYNC();
     };
 
     // ---- fragment reads of k-block kb
@@ -541,6 +564,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             read_rows(lb, wn0, kb, TN, b, lo - TM, hi - TM);
         else
             read_bt(lb, kb, b, lo - TM, hi - TM);
+        DGE_DIAG_SYNC();
     };
     // MFMAs [lo, hi) of one k-block over the TM x TN blocks in serpentine
     // order (row i left to right, row i + 1 right to left), so consecutive
