@@ -575,6 +575,67 @@ def cpu_baseline(A, B, inputs, seconds_target=15.0):
     return res
 
 
+# ------------------------------------------------------------ profiler runs
+
+def _kernel_set_calls(name, dge, inputs, torch):
+    """(label, call) pairs of one workload's kernels on its full-size inputs."""
+    calls = []
+    if name == "square4096":
+        A, B = inputs.square4096("f16")
+        dA, dB = _dev(A, "f16", torch), _dev(B, "f16", torch)
+        C = torch.empty((4096, 4096), dtype=torch.float16, device="cuda")
+        calls.append(("gemm_f16 4096^3", lambda: dge.gemm_f16(dA, dB, C)))
+    elif name == "prefill":
+        for shape in ("attn", "up", "down"):
+            A, q, N, K = inputs.prefill_projection(shape)
+            dA, dq = _dev(A, "f16", torch), torch.from_numpy(q).cuda()
+            w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
+            C = torch.empty((2048, N), dtype=torch.float16, device="cuda")
+            wsz = dge.gemm_workspace_size(2048, N, K, torch.float16)
+            ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda")
+            dge.dequant_q4_f16(dq, N, K, out=w16)
+            calls.append(("dequant_q4_f16 %s" % shape,
+                          lambda dq=dq, N=N, K=K, w16=w16: dge.dequant_q4_f16(dq, N, K, out=w16)))
+            calls.append(("gemm_f16 %s" % shape,
+                          lambda dA=dA, w16=w16, C=C, ws=ws: dge.gemm_f16(dA, w16, C, trans_b=True,
+                                                                         workspace=ws)))
+            calls.append(("gemm_q4_f16 %s" % shape,
+                          lambda dA=dA, dq=dq, N=N, K=K, C=C, ws=ws: dge.gemm_q4_f16(
+                              dA, dq, N, K, C, workspace=ws)))
+    elif name == "skinny":
+        for N in (160, 32):
+            X, W, bias = inputs.tall_skinny(N)
+            dX, dW, db = _dev(X, "f16", torch), _dev(W, "f16", torch), _dev(bias, "f16", torch)
+            C = torch.empty((65536, N), dtype=torch.float16, device="cuda")
+            calls.append(("skinny N=%d" % N, lambda dX=dX, dW=dW, C=C, db=db: dge.gemm_f16(
+                dX, dW, C, epi="bias_gelu", bias=db)))
+    elif name == "decode":
+        _, W = inputs.decode_shape(1)
+        dW = _dev(W, "f16", torch)
+        for M in inputs.DECODE_ROWS:
+            X, _ = inputs.decode_shape(M)
+            dX = _dev(X, "f16", torch)
+            C = torch.empty((M, 4096), dtype=torch.float16, device="cuda")
+            calls.append(("decode M=%d" % M, lambda dX=dX, C=C: dge.gemm_f16(dX, dW, C,
+                                                                             trans_b=True)))
+    return calls
+
+
+KERNEL_SETS = ("square4096", "prefill", "skinny", "decode")
+
+
+def run_kernel_set(name, dge, inputs, torch, steps, warmup):
+    calls = _kernel_set_calls(name, dge, inputs, torch)
+    for label, fn in calls:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_set": name, "call": label, "launches": steps}), flush=True)
+
+
 # ------------------------------------------------------------ main
 
 def main():
@@ -593,6 +654,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only a plain 256 MiB device-to-device copy, 5 times (the reference "
                          "for scaling HBM byte counters)")
+    ap.add_argument("--kernel-set", choices=sorted(KERNEL_SETS),
+                    help="only launch one workload's kernels --steps times each, after "
+                         "--warmup launches, and print their names (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: every GPU box here has one, and the library has "
@@ -602,6 +666,10 @@ def main():
     import torch
     import dense_gemm_engineering_amd.binding as dge
     from dense_gemm_engineering_amd import inputs
+
+    if args.kernel_set:
+        run_kernel_set(args.kernel_set, dge, inputs, torch, args.steps, args.warmup)
+        return
 
     if args.copy_calibration:
         n = 256 << 20

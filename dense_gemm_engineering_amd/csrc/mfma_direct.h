@@ -130,6 +130,14 @@ __device__ inline void lds_dma16_s(const void* sbase, uint32_t voff, DGE_LDS voi
                  "s"(la)
                  : "memory", "m0");
 }
+// One global_load_lds_dword: 4 bytes per lane from sbase + voff to LDS
+// address (l + 4 * lane), with the same wait discipline as lds_dma16.
+__device__ inline void lds_dma4_s(const void* sbase, uint32_t voff, DGE_LDS void* l) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(la)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ inline uint2 ds_read_tr(const DGE_LDS char* p) {
@@ -172,6 +180,24 @@ __device__ inline void interleave_valu() {
         constexpr int w = (R + 1) * NW / NM - R * NW / NM;
         if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);  // LDS writes
         interleave_valu<NM, V, NW, R + 1>();
+    }
+}
+
+// Scheduling pattern of a fused q4 stage's first k-block: each of its NM
+// MFMAs followed by its share of NRD LDS reads (fragments of the next
+// k-block and raw q4 blocks), NV VALU instructions (the decode) and NW LDS
+// writes (the decoded B tile).
+template <int NM, int NRD, int NV, int NW, int R = 0>
+__device__ inline void interleave_q4() {
+    if constexpr (R < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        constexpr int r = (R + 1) * NRD / NM - R * NRD / NM;
+        if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+        constexpr int v = (R + 1) * NV / NM - R * NV / NM;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);
+        constexpr int w = (R + 1) * NW / NM - R * NW / NM;
+        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);
+        interleave_q4<NM, NRD, NV, NW, R + 1>();
     }
 }
 
@@ -379,10 +405,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     static_assert(TRANS_B || RPI_B * BN * 2 == 1024, "whole k-rows per instruction");
 
     // LDS stages: a third one where it fits (the 8-wave 256 x 128 tile, 144 KB)
-    // on the plain path, so each stage's loads have two stages to land
-    constexpr int NBUF = (!Q4 && !SK && MS == 16 && NW == 8 &&
-                          3 * (A_BYTES + B_BYTES) <= 160 * 1024) ? 3 : 2;
-    __shared__ __attribute__((aligned(1024))) char lds[NBUF][A_BYTES + B_BYTES];
+    // so each stage's loads have two stages to land.  With q4 weights each
+    // buffer also holds the stage's raw blocks: a weight row's 64-weight
+    // slice of a stage is two 18-byte blocks, 36 bytes at a 4-byte aligned
+    // address, brought in by dword direct loads with consecutive lanes on
+    // consecutive dwords (a load covers about 7 rows' slices, so it touches
+    // few cache lines) into a row-major image of 36 bytes per row;
+    // 3 x (32 + 16 + 4.75) KB fits the 160 KB.
+    constexpr int NRAW = BN * 9 / 64;                         // raw dword loads per stage
+    constexpr int RAW_BYTES = (NRAW * 256 + 255) / 256 * 256;
+    constexpr bool Q4_3 = Q4 && !SK && MS == 16 && NW == 8 && BN % 64 == 0 &&
+                          3 * (A_BYTES + B_BYTES + RAW_BYTES) <= 160 * 1024;
+    constexpr int NBUF = ((!Q4 && !SK && MS == 16 && NW == 8 &&
+                           3 * (A_BYTES + B_BYTES) <= 160 * 1024) || Q4_3) ? 3 : 2;
+    constexpr int BUF_BYTES = A_BYTES + B_BYTES + (Q4_3 ? RAW_BYTES : 0);
+    __shared__ __attribute__((aligned(1024))) char lds[NBUF][BUF_BYTES];
     __shared__ int sk_flag;  // stream-K: a counter value broadcast to the workgroup
 
     const int tid = threadIdx.x;
@@ -423,6 +460,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     int m0 = 0, n0 = 0, kbeg = 0;
     const char* a_base = nullptr;
     const char* b_base = nullptr;
+    const char* q_base = nullptr;  // fused q4, three stages: the tile's blocks at kbeg
     auto start_tile = [&](int tm0, int tn0, int tk0) __attribute__((always_inline)) {
         m0 = tm0;
         n0 = tn0;
@@ -432,6 +470,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             b_base = (const char*)p.B + ((int64_t)(n0 + 8 * wave * IB) * p.ldb + kbeg) * 2;
         else
             b_base = (const char*)p.B + ((int64_t)(kbeg + RPI_B * wave * IB) * p.ldb + n0) * 2;
+        if constexpr (Q4_3)
+            q_base = (const char*)p.B + 18 * ((int64_t)n0 * (p.K / 32) + kbeg / 32);
     };
     const int64_t a_kstep = BK;                                        // A per stage
     const int64_t b_kstep = TRANS_B ? (int64_t)BK : (int64_t)BK * p.ldb;  // B per stage
@@ -501,6 +541,93 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
             }
         }
         DGE_DIAG_SYNC();
+    };
+
+    // ---- q4 with three stages: raw blocks by direct dword loads, decoded
+    // from LDS by all threads
+    // raw load i of this wave (i < NRW; instruction r = (wave NRW + i) mod
+    // NRAW, the surplus repeating earlier ones with the same bytes into the
+    // same place): lane L fetches dword D = 64 r + L of the stage's image,
+    // dword D % 9 of row D / 9's slice
+    constexpr int NRW = Q4_3 ? (NRAW + NW - 1) / NW : 1;
+    uint32_t raw_off[NRW], raw_lds[NRW];
+    if constexpr (Q4_3) {
+#pragma unroll
+        for (int i = 0; i < NRW; ++i) {
+            const int r = (wave * NRW + i) % NRAW, D = 64 * r + lane;
+            raw_off[i] = (uint32_t)((D / 9) * 18 * (p.K / 32) + 4 * (D % 9));
+            raw_lds[i] = (uint32_t)(A_BYTES + B_BYTES + 256 * r);
+        }
+    }
+    // raw loads [lo, hi) of stage s into buffer buf's raw area
+    auto issue_raw = [&](int buf, int s, int lo, int hi) __attribute__((always_inline)) {
+        if constexpr (Q4_3) {
+            const char* g = q_base + 36 * s;
+#pragma unroll
+            for (int i = 0; i < NRW; ++i) {
+                if (i < lo || i >= hi) continue;
+                lds_dma4_s(g, raw_off[i], (DGE_LDS char*)&lds[buf][0] + raw_lds[i]);
+            }
+            DGE_DIAG_SYNC();
+        }
+    };
+    // the B tile of the stage whose raw blocks sit in buffer buf, decoded into
+    // it: thread task t = (row t % BN, block j and half h from t / BN), eight
+    // code bytes (16 weights) and the scale each.  A wave's lanes take
+    // consecutive rows with the same (j, h): its raw-image reads fall in
+    // distinct banks (a row is 9 dwords, 9 is odd), and each 16-lane group of
+    // its decoded-chunk writes covers 16 rows of one logical chunk, the
+    // pattern the fragment reads of the swizzled layout are conflict-free for.
+    // In two steps: the raw dwords into registers (q4_raw_read, issued a
+    // k-block ahead of their use, ahead of that k-block's fragment reads, so
+    // that waiting for them never waits for the fragments), then the decode
+    // and the LDS writes (q4_decode_write).
+    constexpr int QP = Q4_3 ? (4 * BN + NTHR - 1) / NTHR : 1;  // tasks per thread
+    uint32_t rawv[QP][4];
+    auto q4_raw_read = [&](int buf) __attribute__((always_inline)) {
+        if constexpr (Q4_3) {
+            const DGE_LDS char* raw = (const DGE_LDS char*)&lds[buf][A_BYTES + B_BYTES];
+#pragma unroll
+            for (int pass = 0; pass < QP; ++pass) {
+                const int t = tid + pass * NTHR;
+                const int row = t % BN, j = (t / BN) >> 1, h = (t / BN) & 1;
+                // dword c of the row's 36 bytes
+                const DGE_LDS uint32_t* rr = (const DGE_LDS uint32_t*)(raw + 36 * row);
+                const int c0 = (18 * j + 2 + 8 * h) >> 2;  // dword of the half's first code byte
+                rawv[pass][0] = rr[4 * j];                 // scale: bytes 0-1 or 18-19
+                rawv[pass][1] = rr[c0];
+                rawv[pass][2] = rr[c0 + 1];
+                rawv[pass][3] = rr[min(c0 + 2, 8)];
+            }
+        }
+    };
+    auto q4_decode_write = [&](int buf) __attribute__((always_inline)) {
+        if constexpr (Q4_3) {
+            DGE_LDS char* lb = (DGE_LDS char*)&lds[buf][A_BYTES];
+#pragma unroll
+            for (int pass = 0; pass < QP; ++pass) {
+                const int t = tid + pass * NTHR;
+                const int row = t % BN, j = (t / BN) >> 1, h = (t / BN) & 1;
+                const uint32_t sh = (uint32_t)((18 * j + 2 + 8 * h) & 2) * 8;  // 16: mid-dword start
+                const uint32_t* w = rawv[pass];
+                const uint32_t c01 = __builtin_amdgcn_alignbit(w[2], w[1], sh);  // code bytes 0-3
+                const uint32_t c23 = __builtin_amdgcn_alignbit(w[3], w[2], sh);  // code bytes 4-7
+                const _Float16 d =
+                    __builtin_bit_cast(_Float16, (uint16_t)(j ? w[0] >> 16 : w[0] & 0xFFFFu));
+                const h2v d2 = {d, d};
+                uint32_t o8[8];
+                q4_decode4(c01 & 0x0F0F0F0Fu, d2, o8);             // weights 8h .. 8h + 3
+                q4_decode4(c23 & 0x0F0F0F0Fu, d2, o8 + 2);         // 8h + 4 .. 8h + 7
+                q4_decode4((c01 >> 4) & 0x0F0F0F0Fu, d2, o8 + 4);  // 16 + 8h ..
+                q4_decode4((c23 >> 4) & 0x0F0F0F0Fu, d2, o8 + 6);
+                DGE_LDS char* brow = lb + row * 128;
+                *(DGE_LDS u32x4*)(brow + (((4 * j + h) ^ swz_k<MS>(row)) << 4)) =
+                    (u32x4){o8[0], o8[1], o8[2], o8[3]};
+                *(DGE_LDS u32x4*)(brow + (((4 * j + 2 + h) ^ swz_k<MS>(row)) << 4)) =
+                    (u32x4){o8[4], o8[5], o8[6], o8[7]};
+            }
+            DGE_DIAG_SYNC();
+        }
     };
 
     // ---- fragment reads of k-block kb
@@ -604,7 +731,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // runs best with all 16 after it (2048 x 4096 x 11008: 153.3 us with 4,
     // 147.2 with 12, 145.2 with 16); the fused q4 kernel keeps a quarter (its
     // decode runs between the MFMAs before the barrier)
-    constexpr int TAIL = MS == 16 ? (Q4 ? NMF / 4 : NBUF == 3 ? NMF : NMF >= 32 ? NMF * 3 / 4 : NMF / 4)
+    constexpr int TAIL = MS == 16 ? (Q4 && !Q4_3 ? NMF / 4 : NBUF == 3 ? NMF : NMF >= 32 ? NMF * 3 / 4 : NMF / 4)
                                   : (NMF / 2 > 0 ? NMF / 2 : 1);
 
     // Main loop over the nk stages of the current tile, stage kt in buffer
@@ -613,12 +740,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // Prologue: stages 0 and 1 in flight, wait for stage 0, read its k-block 0.
     auto mainloop = [&](int nk, int par, bool pre) __attribute__((always_inline)) {
     if (!pre) issue_part(par, 0, 0, NDMA);
-    if constexpr (Q4) q4_load(0);
+    if constexpr (Q4 && !Q4_3) q4_load(0);
     issue_part(par ^ 1, nk > 1 ? 1 : 0, 0, NP0);
-    if constexpr (Q4) q4_store(par);
+    if constexpr (Q4 && !Q4_3) q4_store(par);
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((NP0 & 15) | ((NP0 >> 4) << 14)));  // vmcnt(NP0)
     __syncthreads();
-    if constexpr (Q4) q4_load(nk > 1 ? 1 : 0);
+    if constexpr (Q4 && !Q4_3) q4_load(nk > 1 ? 1 : 0);
     read_kblock(par, 0, fa[0], fb[0]);
 
     // Steady state, stage kt (buffer kt & 1), k-blocks 0 .. KB-1 with their
@@ -645,7 +772,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         }
         constexpr int L = (KB - 1) & 1;
         mma_range(fa[L], fb[L], 0, NMF - TAIL);
-        if constexpr (Q4) {
+        if constexpr (Q4 && !Q4_3) {
             // q4: stage kt + 1's B tile (buffer kt + 1 & 1, free since the last
             // barrier), from the blocks loaded a stage ago, decoded between
             // this k-block's MFMAs: each MFMA is followed by a share of the
@@ -665,7 +792,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
 
-        if constexpr (Q4) {
+        if constexpr (Q4 && !Q4_3) {
             issue_part(st, min(kt + 2, nk - 1), 0, NP0);
             q4_load(min(kt + 2, nk - 1));
             read_kblock(st ^ 1, 0, fa[0], fb[0]);
@@ -736,6 +863,76 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     __syncthreads();
     };
 
+    // Main loop of the fused q4 kernel over three LDS stages.  Stage s lives
+    // in buffer s % 3: its A tile comes by direct loads issued after the
+    // barrier that ends stage s - 3 (as in mainloop3), its raw q4 blocks one
+    // stage earlier, after the barrier that ends stage s - 4, into the raw
+    // area of the same buffer (free by then: the blocks of stage s - 3 were
+    // decoded during stage s - 4), and its B tile is decoded from them by all
+    // threads during stage s - 1, between the MFMAs of its first k-block.  The
+    // barrier ending stage s waits for all but the newest group of loads:
+    // that lands A of stage s + 1 and the raw blocks of stage s + 2, which
+    // the next stage decodes.  Stages past the last re-fetch the last one
+    // (never read), so every stage issues the same loads.
+    constexpr int NG = NDMA + NRW;  // loads per wave issued after each barrier
+    auto mainloop3_q4 = [&](int nk) __attribute__((always_inline)) {
+    if constexpr (Q4_3) {
+    const int l1 = min(1, nk - 1), l2 = min(2, nk - 1), l3 = min(3, nk - 1);
+    issue_raw(0, 0, 0, NRW);                                 // raw 0
+    issue_part(0, 0, 0, NDMA);                               // A 0, raw 1
+    issue_raw(1, l1, 0, NRW);
+    issue_part(1, l1, 0, NDMA);                              // A 1, raw 2
+    issue_raw(2, l2, 0, NRW);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (((2 * NG) & 15) | (((2 * NG) >> 4) << 14)));  // raw 0 in
+    __syncthreads();
+    q4_raw_read(0);
+    q4_decode_write(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): raw area 0 read, B 0 written
+    __syncthreads();
+    issue_part(2, l2, 0, NDMA);                              // A 2, raw 3 (raw area 0 is free)
+    issue_raw(0, l3, 0, NRW);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (((2 * NG) & 15) | (((2 * NG) >> 4) << 14)));  // A 0, raw 1 in
+    __syncthreads();
+    q4_raw_read(1);
+    read_kblock(0, 0, fa[0], fb[0]);
+    int st = 0;  // buffer of stage kt
+    for (int kt = 0; kt < nk; ++kt) {
+        const int sn = st == 2 ? 0 : st + 1;  // buffer of stage kt + 1
+        static_assert(KB == 2, "two k-blocks per stage");
+        // k-block 0: its MFMAs, the fragment reads of k-block 1 and the
+        // decode of stage kt + 1's B tile
+        read_kblock(st, 1, fa[1], fb[1]);
+        q4_decode_write(sn);
+        mma_range(fa[0], fb[0], 0, NMF);
+        interleave_q4<NMF, NRD, 36, 2>();
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kt + 1 complete: its A and (decoded) B; raw blocks of stage
+        // kt + 2 landed (vmcnt(NG): only the newest group may be in flight)
+        __builtin_amdgcn_s_waitcnt(0x0070 | ((NG & 15) | ((NG >> 4) << 14)));
+        __syncthreads();
+        // A of stage kt + 3 into buffer st, raw of stage kt + 4 into buffer
+        // sn's raw area, one load per MFMA of k-block 1, with the reads of
+        // stage kt + 1's k-block 0
+        const int la = min(kt + 3, nk - 1), lr = min(kt + 4, nk - 1);
+        // the raw blocks stage kt + 1 decodes (buffer kt + 2), landed by this
+        // barrier, read ahead of the fragments
+        q4_raw_read(sn == 2 ? 0 : sn + 1);
+#pragma unroll
+        for (int r = 0; r < TAIL; ++r) {
+            const int lo = r * NG / TAIL, hi = (r + 1) * NG / TAIL;
+            issue_part(st, la, lo, min(hi, NDMA));
+            issue_raw(sn, lr, max(lo - NDMA, 0), max(hi - NDMA, 0));
+            read_kblock(sn, 0, fa[0], fb[0], r * NRD / TAIL, (r + 1) * NRD / TAIL);
+        }
+        mma_range(fa[1], fb[1], 0, NMF);
+        tail_reads<TAIL, NRD>();
+        st = sn;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    }
+    };
+
     // the fused epilogue of tile (em0, en0), staged through buffer 0
     auto epilogue = [&](int em0, int en0, int split) __attribute__((always_inline)) {
         epilogue_tile_t<DT, BM, BN, WM, WN, MS, TM, TN, A_BYTES + B_BYTES>(
@@ -757,7 +954,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
         const int k0 = split * p.k_per_split;
         start_tile(tm * BM, tn * BN, k0);
         zero_acc();
-        if constexpr (NBUF == 3)
+        if constexpr (Q4_3)
+            mainloop3_q4((min(k0 + p.k_per_split, p.K) - k0) / BK);
+        else if constexpr (NBUF == 3)
             mainloop3((min(k0 + p.k_per_split, p.K) - k0) / BK);
         else
             mainloop((min(k0 + p.k_per_split, p.K) - k0) / BK, 0, false);
