@@ -442,12 +442,14 @@ def bench_decode(dge, inputs, torch, steps, peaks, rotate_bytes=300e6):
         X, _ = inputs.decode_shape(M)
         dX = _dev(X, "f16", torch)
         C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        wsz = dge.gemm_workspace_size(M, N, K, torch.float16)
+        work = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda") if wsz else None
         it = [0]
 
         def run():
             i = it[0] % nset
             it[0] += 1
-            dge.gemm_f16(dX, Ws[i], C, trans_b=True)
+            dge.gemm_f16(dX, Ws[i], C, trans_b=True, workspace=work)
 
         t = time_graph(run, max(steps, nset), torch)
         alg = gemm_alg_bytes(M, N, K, 2, 2)
@@ -616,8 +618,10 @@ def _kernel_set_calls(name, dge, inputs, torch):
             X, _ = inputs.decode_shape(M)
             dX = _dev(X, "f16", torch)
             C = torch.empty((M, 4096), dtype=torch.float16, device="cuda")
-            calls.append(("decode M=%d" % M, lambda dX=dX, C=C: dge.gemm_f16(dX, dW, C,
-                                                                             trans_b=True)))
+            wsz = dge.gemm_workspace_size(M, 4096, 4096, torch.float16)
+            ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda")
+            calls.append(("decode M=%d" % M, lambda dX=dX, C=C, ws=ws: dge.gemm_f16(
+                dX, dW, C, trans_b=True, workspace=ws)))
     return calls
 
 

@@ -623,8 +623,48 @@ bool decode_eligible(const Gemm& g) {
            g.K % 8 == 0 && aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0;
 }
 
-gemm_status_t run_decode(const Gemm& g) {
-    DecodeArgs a;
+// K slices of the split decode schedule for 33 <= M <= 64 rows (0: the
+// one-pass kernel): about one workgroup per CU, each wave of a slice keeping
+// at least one whole k-block.  Measured on a 4096 x 4096 weight (graph
+// replays, HBM-cold): M = 64 20.6 -> 17.9 us with the split, M = 32 14.0 ->
+// 14.8 us (the fixup pass costs more than the X traffic saved), so M <= 32
+// keeps the one-pass kernel.
+int decode_ksplit(int64_t M, int64_t N, int64_t K, int cus) {
+    if (M <= 32 || M > 64 || N % DSPLIT_ROWS != 0 || K % 32 != 0 ||
+        env_int("GEMM_DECODE_SPLIT", 1) == 0)
+        return 0;
+    const int64_t tiles = N / DSPLIT_ROWS;
+    int ks = (int)std::max<int64_t>(1, std::min<int64_t>(8, (cus + tiles / 2) / tiles));
+    while (ks > 1 && K / 32 / ks < DECODE_WAVES) --ks;
+    return ks > 1 ? ks : 0;
+}
+
+size_t decode_ws_bytes(int64_t M, int64_t N, int ks) {
+    return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+gemm_status_t run_decode(const Gemm& g, int cus) {
+    const int ks = decode_ksplit(g.M, g.N, g.K, cus);
+    if (ks > 1 && g.ws && aligned16(g.ws) && g.ws_bytes >= decode_ws_bytes(g.M, g.N, ks)) {
+        DecodeArgs a{};
+        a.X = g.A;
+        a.W = g.B;
+        a.C = g.C;
+        a.ldx = g.lda;
+        a.ldw = g.ldb;
+        a.ldc = g.ldc;
+        a.M = (int)g.M;
+        a.N = (int)g.N;
+        a.K = (int)g.K;
+        a.c_type = g.c_type;
+        a.ep = make_epilogue(g);
+        a.ksplit = ks;
+        a.ws = (float*)g.ws;
+        hipError_t e = launch_decode_split(g.dt, a, g.stream);
+        if (e == hipSuccess) e = launch_splitk_fixup(g.dt, simple_args(g), a.ws, ks, g.stream);
+        return launch_status(e);
+    }
+    DecodeArgs a{};
     a.X = g.A;
     a.W = g.B;
     a.C = g.C;
@@ -666,14 +706,14 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
             return run_mfma(g, tn.tile, 1, dev.cus, 1);
         case GEMM_ALGO_DECODE:
             if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
-            if (g.K > 0 && decode_eligible(g)) return run_decode(g);
+            if (g.K > 0 && decode_eligible(g)) return run_decode(g, dev.cus);
             return run_mfma(g, tn.tile, 1, dev.cus, 1);
         case GEMM_ALGO_STREAMK:
             if (tn.splits > 1) return GEMM_ERR_INVALID_VALUE;
             return run_mfma(g, tn.tile, 0, dev.cus, 1, 1);
         case GEMM_ALGO_AUTO:
             if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && g.K > 0 && decode_eligible(g))
-                return run_decode(g);
+                return run_decode(g, dev.cus);
             if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && skinny_eligible(g) &&
                 g.M >= 8 * g.N && g.M >= 4096 && env_int("GEMM_SKINNY", 1) != 0)
                 return run_skinny(g, dev.cus);
@@ -969,8 +1009,13 @@ gemm_status_t gemm_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_
 
 size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {
     if (M <= 0 || N <= 0 || K <= 0 || dtype < IN_F16 || dtype > IN_F32) return 0;
-    DeviceInfo dev{1, 256};
+    DeviceInfo dev{1, 256, nullptr};
     if (current_device(&dev) != GEMM_OK) dev.cus = 256;
+    // decode shapes (the split decode schedule, used with an N x K weight)
+    if (dtype != IN_F32 && M <= 64) {
+        const int ks = decode_ksplit(M, N, K, dev.cus);
+        if (ks > 1) return decode_ws_bytes(M, N, ks);
+    }
     if (dtype != IN_F32) {
         ColumnSplit cs;
         if (choose_column_split(M, N, K, dtype, dev.cus, (size_t)-1, ~0u,
@@ -985,7 +1030,7 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int dtype) {
 size_t gemm_workspace_size_streamk(int64_t M, int64_t N, int64_t K, int tile) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     if (tile != GEMM_TILE_AUTO && (tile < TILE_256x256 || tile > TILE_LAST)) return 0;
-    DeviceInfo dev{1, 256};
+    DeviceInfo dev{1, 256, nullptr};
     if (current_device(&dev) != GEMM_OK) dev.cus = 256;
     size_t need = 0;
     for (int t = TILE_256x256; t <= TILE_LAST; ++t) {

@@ -34,9 +34,14 @@ struct DecodeArgs {
     int M, N, K;
     int c_type;
     Epilogue ep;
+    // split schedule (gemm_decode_split_kernel): K slices and the fp32
+    // partial sums, ksplit x M x N (ld N)
+    int ksplit;
+    float* ws;
 };
 
 constexpr int DECODE_WAVES = 8;
+constexpr int DPAD = 17;  // floats per 16-wide row of a partial block in LDS
 // k-blocks whose loads are issued together: 16 (a 4096-deep K in one round
 // trip per wave) while the registers allow, 8 for M > 32
 __host__ __device__ constexpr int decode_batch(int mt) { return mt <= 2 ? 16 : 8; }
@@ -45,8 +50,10 @@ __host__ __device__ constexpr int decode_batch(int mt) { return mt <= 2 ? 16 : 8
 // whose clamped rows make every quad read one address anyway.
 template <int DT, int MT, bool XT = true>
 __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeArgs p) {
-    // partial C^T blocks of every wave: [wave][mt][16 n][16 m] fp32
-    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][MT][256];
+    // partial C^T blocks of every wave: [wave][mt][16 n][16 m] fp32, each n
+    // row padded to DPAD floats so that the summation's reads (16 rows of one
+    // column) fall in different banks
+    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][MT][16 * DPAD];
     // each wave's X transpose slot: MT blocks of 16 rows x 4 16-byte chunks
     __shared__ __attribute__((aligned(16))) u32x4 xslot[XT ? DECODE_WAVES : 1][MT][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part[wave][mt][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[mt][e];
+        for (int e = 0; e < 4; ++e) part[wave][mt][(4 * (lane >> 4) + e) * DPAD + (lane & 15)] = acc[mt][e];
     __syncthreads();
 
     // output (m, n0 + j) for t = 16 m + j: 16 consecutive columns per row
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
         const int mt = m >> 4, ml = m & 15;
         float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < DECODE_WAVES; ++w) s += part[w][mt][j * 16 + ml];  // m < 16 MT
+        for (int w = 0; w < DECODE_WAVES; ++w) s += part[w][mt][j * DPAD + ml];  // m < 16 MT
         const int64_t idx = (int64_t)m * p.ldc + n;
         if (p.c_type == OUT_F32) {
             float* c = (float*)p.C + idx;
@@ -141,6 +148,90 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
             __bf16* c = (__bf16*)p.C + idx;
             *c = (__bf16)apply_epilogue<DT>(p.ep, s, p.ep.beta != 0.0f ? (float)*c : 0.0f, n);
         }
+    }
+}
+
+// Split schedule for 33 <= M <= 64 rows (the kernel above re-reads all of X
+// for every 16 weight rows: at M = 64 that is four times the weight's own
+// bytes).  A workgroup owns DSPLIT_ROWS = 64 weight rows and one of ksplit
+// K slices (grid (N / 64) x ksplit, 256 workgroups for N = 4096 with ksplit
+// = 4); its 8 waves split the slice's k-blocks.  Each wave loads, per
+// k-block, the four 16-row weight fragments and the MT X fragments straight
+// into MFMA operand registers (16 bytes per lane) and applies every X
+// fragment to all four weight blocks, so X crosses from L2 once per
+// workgroup and slice: as many bytes as the weight.  The 8 waves' partial
+// C^T blocks are summed through LDS in wave order and the workgroup writes
+// its fp32 partial of the slice to ws[slice][m][n]; the split-K fixup sums
+// the slices in slice order and applies the epilogue, so the result does
+// not depend on timing.
+constexpr int DSPLIT_ROWS = 64;
+constexpr int DSPLIT_BATCH = 4;  // k-blocks whose loads are issued together
+
+template <int DT, int MT>
+__global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(DecodeArgs p) {
+    constexpr int NB = DSPLIT_ROWS / 16;  // weight blocks per workgroup
+    // partial C^T blocks [wave][nb][mt][16 n x 16 m]
+    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][NB][MT][16 * DPAD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ntile = p.N / DSPLIT_ROWS;
+    const int nb_i = blockIdx.x % ntile, ks = blockIdx.x / ntile;
+    const int n0 = nb_i * DSPLIT_ROWS;
+    const int nkb = p.K / 32;
+    const int s0 = ks * nkb / p.ksplit, s1 = (ks + 1) * nkb / p.ksplit;  // the slice's k-blocks
+    const int kb0 = s0 + wave * (s1 - s0) / DECODE_WAVES;
+    const int kb1 = s0 + (wave + 1) * (s1 - s0) / DECODE_WAVES;
+    const int kch = 8 * (lane >> 4);  // this lane's k offset within a k-block
+    const char* wrow[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        wrow[b] = (const char*)p.W + ((int64_t)(n0 + 16 * b + (lane & 15)) * p.ldw + kch) * 2;
+    const char* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        xrow[mt] = (const char*)p.X + ((int64_t)min(16 * mt + (lane & 15), p.M - 1) * p.ldx + kch) * 2;
+
+    f32x4 acc[NB][MT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[b][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kb = kb0; kb < kb1; kb += DSPLIT_BATCH) {
+        u32x4 wf[DSPLIT_BATCH][NB], xf[DSPLIT_BATCH][MT];
+#pragma unroll
+        for (int i = 0; i < DSPLIT_BATCH; ++i) {
+            const bool in = kb + i < kb1;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                wf[i][b] = in ? load16(wrow[b] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                xf[i][mt] = in ? load16(xrow[mt] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < DSPLIT_BATCH; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[b][mt], wf[i][b], xf[i][mt]);
+    }
+    // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each block
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                part[wave][b][mt][(4 * (lane >> 4) + e) * DPAD + (lane & 15)] = acc[b][mt][e];
+    __syncthreads();
+    // the slice's partial (m, n0 + j), t = 64 m + j: 64 consecutive columns per row
+    float* ws = p.ws + (int64_t)ks * p.M * p.N;
+    for (int t = tid; t < DSPLIT_ROWS * p.M; t += DECODE_WAVES * 64) {
+        const int m = t / DSPLIT_ROWS, j = t % DSPLIT_ROWS;
+        const int b = j >> 4, nl = j & 15, mt = m >> 4, ml = m & 15;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < DECODE_WAVES; ++w) sum += part[w][b][mt][nl * DPAD + ml];
+        ws[(int64_t)m * p.N + n0 + j] = sum;
     }
 }
 

@@ -39,6 +39,20 @@ hipError_t launch_lds_tiled(int dt, const SimpleArgs& a, hipStream_t s) {
 template <int DT>
 static hipError_t fixup_dt(const SimpleArgs& a, const float* ws, int splits, hipStream_t s) {
     const int64_t total = (int64_t)a.M * a.N;
+    const int ob = a.c_type == OUT_F32 ? 4 : 2;
+    if (a.N % 4 == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)a.C & (4 * ob - 1)) == 0 &&
+        (a.ldc * ob) % (4 * ob) == 0) {
+        int64_t blocks = (total / 4 + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        const dim3 g((unsigned)blocks), b(256);
+        if (a.c_type == OUT_F16)
+            hipLaunchKernelGGL((splitk_fixup4_kernel<DT, OUT_F16>), g, b, 0, s, a, ws, splits);
+        else if (a.c_type == OUT_BF16)
+            hipLaunchKernelGGL((splitk_fixup4_kernel<DT, OUT_BF16>), g, b, 0, s, a, ws, splits);
+        else
+            hipLaunchKernelGGL((splitk_fixup4_kernel<DT, OUT_F32>), g, b, 0, s, a, ws, splits);
+        return hipGetLastError();
+    }
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((splitk_fixup_kernel<DT>), dim3((unsigned)blocks), dim3(256), 0, s, a, ws,

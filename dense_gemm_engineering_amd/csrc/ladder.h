@@ -133,4 +133,36 @@ __global__ __launch_bounds__(256) void splitk_fixup_kernel(SimpleArgs p, const f
     }
 }
 
+// The same fixup, four consecutive columns per thread: 16-byte partial
+// loads, one 8- or 16-byte store (N % 4 == 0, the workspace 16-byte aligned,
+// C rows and the 4-column groups aligned to their store size).  Each group
+// is summed in the same slice order as above.
+template <int DT, int OT>
+__global__ __launch_bounds__(256) void splitk_fixup4_kernel(SimpleArgs p, const float* ws,
+                                                            int splits) {
+    typedef typename OutType<OT>::T T;
+    const int64_t total = (int64_t)p.M * p.N, groups = total / 4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+        const int64_t idx = 4 * g;
+        f32x4 s = *(const f32x4*)(ws + idx);
+        for (int sp = 1; sp < splits; ++sp) s += *(const f32x4*)(ws + sp * total + idx);
+        const int row = (int)(idx / p.N), col = (int)(idx % p.N);
+        T* c = (T*)p.C + (int64_t)row * p.ldc + col;
+        T o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float old = p.ep.beta != 0.0f ? OutType<OT>::to_f32(c[e]) : 0.0f;
+            o[e] = OutType<OT>::from_f32(apply_epilogue<DT>(p.ep, s[e], old, col + e));
+        }
+        if constexpr (OutType<OT>::BYTES == 4)
+            *(f32x4*)c = (f32x4){o[0], o[1], o[2], o[3]};
+        else
+            *(uint2*)c = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16),
+                                    (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16));
+    }
+}
+
 }  // namespace dge

@@ -130,7 +130,12 @@ typedef enum {
                                  problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO uses it
                                  whenever eligible ("Matrix Multiplication: The
                                  Operation Behind Modern AI", "The shape a language
-                                 model actually runs"). */
+                                 model actually runs").  For 33 <= M <= 64 with
+                                 N % 64 == 0 and K % 32 == 0 it also splits K over
+                                 workgroups (64 weight rows each, X read once per
+                                 workgroup) when the workspace holds the fp32
+                                 partials (gemm_workspace_size gives the bytes); the
+                                 split-K fixup sums them in slice order. */
     GEMM_ALGO_STREAMK = 7     /* persistent stream-K schedule of the direct-to-LDS
                                  kernels ("Optimizing GEMMs using tcgen05 - Part 2",
                                  §8: stream-K for the tail and a persistent kernel

@@ -77,3 +77,57 @@ def test_decode_misaligned_falls_back():
     C = dge.gemm_ex(to_dev(X, "f16"), dW, trans_b=True, out_dtype=torch.float32, algo="decode")
     torch.cuda.synchronize()
     assert_bits(C, T)
+
+
+def _split_ws(M, N, K, dtype):
+    n = dge.gemm_workspace_size(M, N, K, {"f16": torch.float16, "bf16": torch.bfloat16}[dtype])
+    return torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(33, 64, 4096), (32, 4096, 4096), (48, 1088, 11008),
+                                   (64, 4096, 4096), (64, 128, 8192), (40, 192, 256)])
+def test_decode_split_integer_exact_and_deterministic(M, N, K, dtype):
+    # with a workspace, 33 <= M <= 64 splits K over workgroups of 64 weight
+    # rows (uneven slices at K = 11008); the fp32 partials are summed in slice
+    # order, so integer inputs give the oracle's bits on every run
+    X, W = _ints((M, K), dtype, 6400 + M), _ints((N, K), dtype, 6500 + N)
+    T, _ = oracle.gemm(X, W, dtype, trans_b=True, want_U=False)
+    ws = _split_ws(M, N, K, dtype)
+    outs = []
+    for _ in range(2):
+        C = dge.gemm_ex(to_dev(X, dtype), to_dev(W, dtype), trans_b=True,
+                        out_dtype=torch.float32, algo="decode", workspace=ws)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what="%dx%dx%d %s" % (M, N, K, dtype))
+        outs.append(C.cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_decode_split_epilogue():
+    M, N, K = 40, 512, 4096
+    r = np.random.Generator(np.random.PCG64(6600))
+    X = inputs.to_bits(r.normal(0, 1, (M, K)), "f16")
+    W = inputs.to_bits(r.normal(0, 1 / np.sqrt(K), (N, K)), "f16")
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), "f16")
+    cold_bits = inputs.to_bits(r.normal(0, 1, (M, N)), "f16")
+    C = to_dev(cold_bits, "f16")
+    dge.gemm_f16(to_dev(X, "f16"), to_dev(W, "f16"), C, trans_b=True, alpha=0.5, beta=-1.0,
+                 epi="bias_gelu", bias=to_dev(bias_bits, "f16"), workspace=_split_ws(M, N, K, "f16"))
+    torch.cuda.synchronize()
+    T, U = oracle.gemm(X, W, "f16", trans_b=True, alpha=0.5, beta=-1.0,
+                       C_old=oracle.decode(cold_bits, "f16"), epi="bias_gelu",
+                       bias=oracle.decode(bias_bits, "f16"))
+    assert_close(C, T, U, alpha=0.5)
+
+
+@pytest.mark.parametrize("M", inputs.DECODE_ROWS)
+def test_decode_workload_4096_with_workspace(M):
+    # the launch configuration the benchmark times (workspace from
+    # gemm_workspace_size: the split schedule for M = 64)
+    X, W = inputs.decode_shape(M)
+    C = dge.gemm_f16(to_dev(X, "f16"), to_dev(W, "f16"), trans_b=True, out_dtype=torch.float16,
+                     workspace=_split_ws(M, 4096, 4096, "f16"))
+    torch.cuda.synchronize()
+    T, U = oracle.gemm(X, W, "f16", trans_b=True)
+    assert_close(C, T, U, what="M=%d" % M)
