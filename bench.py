@@ -622,10 +622,24 @@ def _kernel_set_calls(name, dge, inputs, torch):
             ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda")
             calls.append(("decode M=%d" % M, lambda dX=dX, C=C, ws=ws: dge.gemm_f16(
                 dX, dW, C, trans_b=True, workspace=ws)))
+    elif name == "streamk":
+        shapes = {"square_4096": (4096, 4096, 4096), "up": (2048, 11008, 4096),
+                  "attn": (2048, 4096, 4096), "down": (2048, 4096, 11008)}
+        for label, (M, N, K) in shapes.items():
+            A = torch.randn(M, K, device="cuda", dtype=torch.float16) / K ** 0.5
+            B = torch.randn(N, K, device="cuda", dtype=torch.float16) / K ** 0.5
+            C = torch.empty(M, N, device="cuda", dtype=torch.float16)
+            n = max(dge.gemm_workspace_size(M, N, K, torch.float16),
+                    dge.gemm_workspace_size_streamk(M, N, K))
+            ws = torch.empty(n // 4 + 1, dtype=torch.float32, device="cuda")
+            calls.append(("default %s" % label, lambda A=A, B=B, C=C, ws=ws: dge.gemm_f16(
+                A, B, C, trans_b=True, workspace=ws)))
+            calls.append(("streamk %s" % label, lambda A=A, B=B, C=C, ws=ws: dge.gemm_ex(
+                A, B, C, trans_b=True, workspace=ws, algo="streamk")))
     return calls
 
 
-KERNEL_SETS = ("square4096", "prefill", "skinny", "decode")
+KERNEL_SETS = ("square4096", "prefill", "skinny", "decode", "streamk")
 
 
 def run_kernel_set(name, dge, inputs, torch, steps, warmup):
