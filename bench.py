@@ -281,8 +281,10 @@ def bench_headline(dge, inputs, torch, steps, windows, repeats, warmup, dtype, s
     wins = {k: [] for k in legs}
     clocks = {"gemm_clock": [], "mfma_only": []}
     names = list(legs)
+    order = []
     for _ in range(repeats):
         for k in [names[i] for i in rng.permutation(len(names))]:
+            order.append(k)
             fn = legs[k]
             t0 = time.perf_counter()
             fn()
@@ -293,7 +295,36 @@ def bench_headline(dge, inputs, torch, steps, windows, repeats, warmup, dtype, s
             if k in clocks:
                 clocks[k].append(clock_of(clk if k == "gemm_clock" else clk_mfma))
     del dA, dB, dAb, dBb, C, C32, work, dBt
-    return wins, clocks, A, B
+    return wins, clocks, A, B, order
+
+
+def bench_ksweep(dge, torch, steps, Ks=(1024, 2048, 4096, 8192)):
+    """M = N = 4096 fp16 GEMMs (K x N B, fp16 out) over K: per-launch time,
+    the engine clock and the spread of workgroup start and end times from the
+    kernel's clock records, and a least-squares line time = fixed + per-stage
+    x stages whose intercept is the per-launch cost that does not scale with
+    K (launch, prologue, epilogue store burst)."""
+    out = {}
+    for K in Ks:
+        a = (torch.randn(4096, K, device="cuda") / 64).half()
+        b = (torch.randn(K, 4096, device="cuda") / 64).half()
+        C = torch.empty(4096, 4096, device="cuda", dtype=torch.float16)
+        clk = torch.zeros(4 * 1024, dtype=torch.int64, device="cuda")
+        t = time_leg(lambda: dge.gemm_f16(a, b, C), steps, torch, windows=5, warm_seconds=0.2)
+        dge.probe_clock(a, b, C, clk)
+        torch.cuda.synchronize()
+        c = clk.view(-1, 4)[:256].cpu().numpy().astype(np.float64)
+        st, en = (c[:, 1] - c[:, 1].min()) / 100.0, (c[:, 3] - c[:, 1].min()) / 100.0
+        out["K%d" % K] = {"us": t["us"], "sclk_mhz": float(np.mean((c[:, 2] - c[:, 0]) /
+                                                                   (c[:, 3] - c[:, 1]) * 100.0)),
+                          "wg_start_max_us": float(st.max()), "wg_end_min_us": float(en.min()),
+                          "wg_end_max_us": float(en.max())}
+        del a, b, C
+    x = np.array([K / 64 for K in Ks])
+    y = np.array([out["K%d" % K]["us"] for K in Ks])
+    slope, icpt = np.polyfit(x, y, 1)
+    out["fit"] = {"fixed_us": float(icpt), "us_per_stage": float(slope)}
+    return out
 
 
 def bench_stream_peaks(dge, torch, windows=5, nbytes=1 << 30, grids=(2048, 4096, 8192, 16384, 32768)):
@@ -703,8 +734,8 @@ def main():
     dge.gemm_init()
     M = N = K = 4096
     flops = gemm_flops(M, N, K)
-    wins, clocks, A, B = bench_headline(dge, inputs, torch, args.steps, args.windows,
-                                        args.repeats, args.warmup, args.dtype)
+    wins, clocks, A, B, order = bench_headline(dge, inputs, torch, args.steps, args.windows,
+                                               args.repeats, args.warmup, args.dtype)
     head = summarize(wins["gemm"], args.steps)
     ms_per_step = head["wall_us"] * 1e-3
     value = flops / (head["wall_us"] * 1e-6) / 1e12
@@ -758,11 +789,16 @@ def main():
                                 mfma_frac=flops / legs["bf16"]["us"] / 1e6 / PEAK["bf16"]),
             "gemm_with_clock_records": legs["gemm_clock"],
             "mfma_only_probe": legs["mfma_only"],
+            # the order the legs ran in (warm-up calls, a settling period and
+            # the windows of each); the fp16-out, fp32-out and clock-record
+            # legs launch the same kernel
+            "order": order,
         },
         "hbm_peaks": peaks,
     }
     if not args.no_extra:
         extra_steps = max(10, min(args.steps, 30))
+        line["ksweep_4096"] = bench_ksweep(dge, torch, extra_steps)
         line["prefill_2048"] = bench_prefill(dge, inputs, torch, extra_steps, peaks)
         line["prefill_kquant"] = bench_kquant(dge, inputs, torch, extra_steps,
                                               line["prefill_2048"], peaks)
