@@ -273,6 +273,20 @@ def bench_headline(dge, inputs, torch, steps, windows, repeats, warmup, dtype, s
         "gemm_clock": lambda: dge.probe_clock(dA, dB, C, clk),
         "mfma_only": lambda: dge.probe_mfma(dA, dBt, 128, probe_out, clk_mfma),
     }
+    # launches per leg invocation, in launch order, so that a kernel trace of
+    # this run can be split by leg
+    launch_log = []
+
+    def counted(k, fn):
+        def call():
+            if launch_log and launch_log[-1][0] == k:
+                launch_log[-1][1] += 1
+            else:
+                launch_log.append([k, 1])
+            fn()
+        return call
+
+    legs = {k: counted(k, fn) for k, fn in legs.items()}
     for fn in legs.values():
         for _ in range(warmup):
             fn()
@@ -295,7 +309,7 @@ def bench_headline(dge, inputs, torch, steps, windows, repeats, warmup, dtype, s
             if k in clocks:
                 clocks[k].append(clock_of(clk if k == "gemm_clock" else clk_mfma))
     del dA, dB, dAb, dBb, C, C32, work, dBt
-    return wins, clocks, A, B, order
+    return wins, clocks, A, B, order, launch_log
 
 
 def bench_ksweep(dge, torch, steps, Ks=(1024, 2048, 4096, 8192)):
@@ -734,7 +748,7 @@ def main():
     dge.gemm_init()
     M = N = K = 4096
     flops = gemm_flops(M, N, K)
-    wins, clocks, A, B, order = bench_headline(dge, inputs, torch, args.steps, args.windows,
+    wins, clocks, A, B, order, launch_log = bench_headline(dge, inputs, torch, args.steps, args.windows,
                                                args.repeats, args.warmup, args.dtype)
     head = summarize(wins["gemm"], args.steps)
     ms_per_step = head["wall_us"] * 1e-3
@@ -793,6 +807,7 @@ def main():
             # the windows of each); the fp16-out, fp32-out and clock-record
             # legs launch the same kernel
             "order": order,
+            "launch_log": launch_log,
         },
         "hbm_peaks": peaks,
     }
