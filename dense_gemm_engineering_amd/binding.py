@@ -35,7 +35,8 @@ EXPORTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_ex", "gemm_ex_noalloc", "d
            "gemm_workspace_size", "gemm_workspace_size_splits", "gemm_workspace_size_streamk",
            "gemm_status_string", "gemm_init",
            # measurement probes (include/gemm_probe.h)
-           "gemm_probe_clock", "gemm_probe_mfma", "gemm_probe_read", "gemm_probe_copy")
+           "gemm_probe_clock", "gemm_probe_phases", "gemm_probe_mfma", "gemm_probe_read",
+           "gemm_probe_copy")
 PROBE_MFMA_GRID = 256
 
 
@@ -108,6 +109,9 @@ def lib():
         L.gemm_init.restype = i32
         L.gemm_probe_clock.argtypes = [i32] + gemm_args[:-3] + [vp, i64, vp]
         L.gemm_probe_clock.restype = i32
+        L.gemm_probe_phases.argtypes = [i32, i64, i64, i64, vp, i64, vp, i64, i32, vp, i64, i32,
+                                        i32, vp, vp, sz, vp, i64, vp]
+        L.gemm_probe_phases.restype = i32
         L.gemm_probe_mfma.argtypes = [i32, vp, i64, vp, i64, i64, i64, i32, vp, vp, vp]
         L.gemm_probe_mfma.restype = i32
         L.gemm_probe_read.argtypes = [vp, sz, i32, vp, vp]
@@ -300,6 +304,22 @@ def probe_clock(A, B, C, clk, *, trans_b=False, stream=None):
                                   _ld(B, "B"), int(bool(trans_b)), 0.0, _ptr(C), _ld(C, "C"),
                                   OUT[C.dtype], 0, None, _ptr(clk), clk.numel() // 4,
                                   _stream(stream)), "gemm_probe_clock")
+    return C
+
+
+def probe_phases(A, B, C, rec, *, trans_b=False, epi="none", bias=None, workspace=None,
+                 stream=None):
+    """The automatic GEMM with phase records (the split decode schedule):
+    rec is an int64 device tensor of 4 real-time counter values per
+    workgroup."""
+    M, N, K, C = _prepare(A, B, C, trans_b, C.dtype)
+    _check(lib().gemm_probe_phases(IN[A.dtype], M, N, K, _ptr(A), _ld(A, "A"), _ptr(B),
+                                   _ld(B, "B"), int(bool(trans_b)), _ptr(C), _ld(C, "C"),
+                                   OUT[C.dtype], EPI[epi], _ptr(bias), _ptr(workspace),
+                                   0 if workspace is None else
+                                   workspace.numel() * workspace.element_size(),
+                                   _ptr(rec), rec.numel() // 4,
+                                   _stream(stream)), "gemm_probe_phases")
     return C
 
 

@@ -623,14 +623,14 @@ bool decode_eligible(const Gemm& g) {
            g.K % 8 == 0 && aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0;
 }
 
-// K slices of the split decode schedule for 33 <= M <= 64 rows (0: the
+// K slices of the split decode schedule for 17 <= M <= 64 rows (0: the
 // one-pass kernel): about one workgroup per CU, each wave of a slice keeping
 // at least one whole k-block.  Measured on a 4096 x 4096 weight (graph
-// replays, HBM-cold): M = 64 20.6 -> 17.9 us with the split, M = 32 14.0 ->
-// 14.8 us (the fixup pass costs more than the X traffic saved), so M <= 32
-// keeps the one-pass kernel.
+// replays, HBM-cold), split + fixup against one pass: M = 17 12.0 / 12.6 us,
+// M = 32 12.8 / 15.3, M = 48 12.5 / 18.9, M = 64 14.6 / 21.8; M <= 16 keeps
+// the one-pass kernel (its X traffic is no larger than the weight's).
 int decode_ksplit(int64_t M, int64_t N, int64_t K, int cus) {
-    if (M <= 32 || M > 64 || N % DSPLIT_ROWS != 0 || K % 32 != 0 ||
+    if (M <= 16 || M > 64 || N % DSPLIT_ROWS != 0 || K % 32 != 0 ||
         env_int("GEMM_DECODE_SPLIT", 1) == 0)
         return 0;
     const int64_t tiles = N / DSPLIT_ROWS;
@@ -643,27 +643,7 @@ size_t decode_ws_bytes(int64_t M, int64_t N, int ks) {
     return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-gemm_status_t run_decode(const Gemm& g, int cus) {
-    const int ks = decode_ksplit(g.M, g.N, g.K, cus);
-    if (ks > 1 && g.ws && aligned16(g.ws) && g.ws_bytes >= decode_ws_bytes(g.M, g.N, ks)) {
-        DecodeArgs a{};
-        a.X = g.A;
-        a.W = g.B;
-        a.C = g.C;
-        a.ldx = g.lda;
-        a.ldw = g.ldb;
-        a.ldc = g.ldc;
-        a.M = (int)g.M;
-        a.N = (int)g.N;
-        a.K = (int)g.K;
-        a.c_type = g.c_type;
-        a.ep = make_epilogue(g);
-        a.ksplit = ks;
-        a.ws = (float*)g.ws;
-        hipError_t e = launch_decode_split(g.dt, a, g.stream);
-        if (e == hipSuccess) e = launch_splitk_fixup(g.dt, simple_args(g), a.ws, ks, g.stream);
-        return launch_status(e);
-    }
+DecodeArgs decode_args(const Gemm& g) {
     DecodeArgs a{};
     a.X = g.A;
     a.W = g.B;
@@ -676,7 +656,23 @@ gemm_status_t run_decode(const Gemm& g, int cus) {
     a.K = (int)g.K;
     a.c_type = g.c_type;
     a.ep = make_epilogue(g);
-    return launch_status(launch_decode(g.dt, a, g.stream));
+    return a;
+}
+
+gemm_status_t run_decode(const Gemm& g, int cus) {
+    const int ks = decode_ksplit(g.M, g.N, g.K, cus);
+    if (ks > 1 && g.ws && aligned16(g.ws) && g.ws_bytes >= decode_ws_bytes(g.M, g.N, ks)) {
+        DecodeArgs a = decode_args(g);
+        a.ksplit = ks;
+        a.ws = (float*)g.ws;
+        if (g.clk && g.clk_cap < g.N / DSPLIT_ROWS * ks) return GEMM_ERR_NOT_SUPPORTED;
+        a.rec = g.clk;
+        hipError_t e = launch_decode_split(g.dt, a, g.stream);
+        if (e == hipSuccess) e = launch_splitk_fixup(g.dt, simple_args(g), a.ws, ks, g.stream);
+        return launch_status(e);
+    }
+    if (g.clk) return GEMM_ERR_NOT_SUPPORTED;
+    return launch_status(launch_decode(g.dt, decode_args(g), g.stream));
 }
 
 gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
@@ -830,6 +826,26 @@ gemm_status_t gemm_probe_clock(gemm_in_t in_type, int64_t M, int64_t N, int64_t 
     DeviceInfo dev;
     if ((st = current_device(&dev)) != GEMM_OK) return st;
     return run_mfma(g, GEMM_TILE_AUTO, 0, dev.cus, 1);
+}
+
+gemm_status_t gemm_probe_phases(gemm_in_t in_type, int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                int trans_b, void* C, int64_t ldc, gemm_out_t c_type,
+                                gemm_epilogue_t epi, const void* bias, void* workspace,
+                                size_t workspace_bytes, unsigned long long* rec,
+                                int64_t rec_entries, void* stream) {
+    if (!rec || rec_entries <= 0 || ((uintptr_t)rec & 15)) return GEMM_ERR_INVALID_VALUE;
+    Gemm g = make_gemm((int)in_type, M, N, K, 1.0f, A, lda, B, ldb, trans_b, 0.0f, C, ldc,
+                       c_type, epi, bias, workspace, workspace_bytes, stream);
+    g.clk = rec;
+    g.clk_cap = rec_entries;
+    gemm_status_t st = validate(g);
+    if (st != GEMM_OK || g.M == 0 || g.N == 0) return st;
+    if (g.K == 0) return GEMM_ERR_NOT_SUPPORTED;
+    DeviceInfo dev;
+    if ((st = current_device(&dev)) != GEMM_OK) return st;
+    if (decode_eligible(g) && decode_ksplit(g.M, g.N, g.K, dev.cus) > 1) return run_decode(g, dev.cus);
+    return GEMM_ERR_NOT_SUPPORTED;
 }
 
 gemm_status_t gemm_probe_mfma(gemm_in_t in_type, const void* A, int64_t lda, const void* B,

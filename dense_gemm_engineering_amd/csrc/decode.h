@@ -35,9 +35,11 @@ struct DecodeArgs {
     int c_type;
     Epilogue ep;
     // split schedule (gemm_decode_split_kernel): K slices and the fp32
-    // partial sums, ksplit x M x N (ld N)
+    // partial sums (ksplit x M x N, ld N); rec (may be null): 4 real-time
+    // counter values per workgroup
     int ksplit;
     float* ws;
+    unsigned long long* rec;
 };
 
 constexpr int DECODE_WAVES = 8;
@@ -151,28 +153,43 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
     }
 }
 
-// Split schedule for 33 <= M <= 64 rows (the kernel above re-reads all of X
+// Split schedule for 17 <= M <= 64 rows (the kernel above re-reads all of X
 // for every 16 weight rows: at M = 64 that is four times the weight's own
 // bytes).  A workgroup owns DSPLIT_ROWS = 64 weight rows and one of ksplit
 // K slices (grid (N / 64) x ksplit, 256 workgroups for N = 4096 with ksplit
-// = 4); its 8 waves split the slice's k-blocks.  Each wave loads, per
-// k-block, the four 16-row weight fragments and the MT X fragments straight
-// into MFMA operand registers (16 bytes per lane) and applies every X
-// fragment to all four weight blocks, so X crosses from L2 once per
-// workgroup and slice: as many bytes as the weight.  The 8 waves' partial
-// C^T blocks are summed through LDS in wave order and the workgroup writes
-// its fp32 partial of the slice to ws[slice][m][n]; the split-K fixup sums
-// the slices in slice order and applies the epilogue, so the result does
-// not depend on timing.
+// = 4), so X crosses from L2 once per workgroup and slice: as many bytes as
+// the weight.  Its 8 waves split the slice's k-blocks.
+//
+//  * Weight loads are coalesced: a wave takes its k-blocks in spans of
+//    DSPAN = 4 (128 k, 256 bytes of a row), and each 16-byte load
+//    instruction covers 4 whole rows x 256 bytes (lane L: row L / 16,
+//    16-byte unit L % 16).  The MFMA operand layout (lane L: row L % 16) puts
+//    16 rows under every instruction and 4 rows under every lane quad, and
+//    the memory pipeline then moves the same bytes at about half the rate
+//    (M = 64 on a 4096 x 4096 weight: 7.7 -> 4.4 us median for a wave's
+//    loads).  Each 16-row group goes through a 4 KB slot of the wave's own
+//    LDS (16-byte unit u of row r at r * 16 + (u ^ r): conflict-free both
+//    ways) into operand layout.
+//  * The 8 waves' partial C^T blocks are summed through LDS in wave order
+//    (the slots alias each wave's own part of that buffer) and written to
+//    ws[slice][m][n]; the split-K fixup sums the slices in slice order and
+//    applies the epilogue, so the result does not depend on timing.  (A
+//    last-arriving workgroup finishing C in this launch was slower here: the
+//    device-scope stores, counter and loads it needs cost ~4 round trips of
+//    ~1.5 us to the memory side, against ~2.7 us for the fixup launch.)
 constexpr int DSPLIT_ROWS = 64;
-constexpr int DSPLIT_BATCH = 4;  // k-blocks whose loads are issued together
+constexpr int DSPAN = 4;  // k-blocks per load span
 
 template <int DT, int MT>
 __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(DecodeArgs p) {
     constexpr int NB = DSPLIT_ROWS / 16;  // weight blocks per workgroup
-    // partial C^T blocks [wave][nb][mt][16 n x 16 m]
+    // partial C^T blocks [wave][nb][mt][16 n x 16 m]; during the main loop
+    // each wave's part holds its transpose slot
     __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][NB][MT][16 * DPAD];
+    static_assert(NB * MT * 16 * DPAD * 4 >= 16 * 16 * 16, "transpose slot fits a wave's part");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned long long t_start = 0, t_land = 0;
+    if (p.rec && tid == 0) t_start = __builtin_amdgcn_s_memrealtime();
     const int ntile = p.N / DSPLIT_ROWS;
     const int nb_i = blockIdx.x % ntile, ks = blockIdx.x / ntile;
     const int n0 = nb_i * DSPLIT_ROWS;
@@ -180,39 +197,92 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
     const int s0 = ks * nkb / p.ksplit, s1 = (ks + 1) * nkb / p.ksplit;  // the slice's k-blocks
     const int kb0 = s0 + wave * (s1 - s0) / DECODE_WAVES;
     const int kb1 = s0 + (wave + 1) * (s1 - s0) / DECODE_WAVES;
-    const int kch = 8 * (lane >> 4);  // this lane's k offset within a k-block
-    const char* wrow[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-        wrow[b] = (const char*)p.W + ((int64_t)(n0 + 16 * b + (lane & 15)) * p.ldw + kch) * 2;
-    const char* xrow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        xrow[mt] = (const char*)p.X + ((int64_t)min(16 * mt + (lane & 15), p.M - 1) * p.ldx + kch) * 2;
+    const int lr = lane >> 4, lu = lane & 15;  // load layout: row within 4, 16-byte unit
+    const int orow = lane & 15, ochunk = lane >> 4;  // operand layout: row, 8-element chunk
+    u32x4* slot = (u32x4*)&part[wave][0][0][0];
 
     f32x4 acc[NB][MT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[b][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int kb = kb0; kb < kb1; kb += DSPLIT_BATCH) {
-        u32x4 wf[DSPLIT_BATCH][NB], xf[DSPLIT_BATCH][MT];
+
+    // per-lane byte offsets: W row n0 + 16 g + 4 j + lr is the uniform
+    // (16 g + 4 j) x ldw on top of lr x ldw.  X (L2-resident, shared by the
+    // slice's workgroups) is loaded straight in operand layout: a coalesced
+    // load and transpose measured the same.  Its rows are clamped to M - 1
+    // (rows past M feed only outputs that are never stored).
+    const uint32_t wlane = (uint32_t)(lr * p.ldw * 2 + 16 * lu);
+    uint32_t xlane[MT];
 #pragma unroll
-        for (int i = 0; i < DSPLIT_BATCH; ++i) {
-            const bool in = kb + i < kb1;
+    for (int g = 0; g < MT; ++g)
+        xlane[g] = (uint32_t)((min(16 * g + orow, p.M - 1) * p.ldx + 8 * ochunk) * 2);
+    const char* wtile = (const char*)p.W + (int64_t)n0 * p.ldw * 2;
+
+    // whole spans
+    int kbs = kb0;
+    for (; kbs + DSPAN <= kb1; kbs += DSPAN) {
+        u32x4 rw[NB][4], xf[MT][DSPAN];
+        const char* wk = wtile + (int64_t)kbs * 64;
+        const char* xk = (const char*)p.X + (int64_t)kbs * 64;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                wf[i][b] = in ? load16(wrow[b] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+        for (int g = 0; g < NB; ++g) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                xf[i][mt] = in ? load16(xrow[mt] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
+            for (int j = 0; j < 4; ++j) rw[g][j] = load16(wk + (int64_t)(16 * g + 4 * j) * p.ldw * 2 + wlane);
+            if (g < MT) {
+#pragma unroll
+                for (int kb = 0; kb < DSPAN; ++kb) xf[g][kb] = load16(xk + xlane[g] + kb * 64);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (p.rec && tid == 0 && kbs == kb0) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            t_land = __builtin_amdgcn_s_memrealtime();
+        }
+        // 16-row group -> operand fragments of its DSPAN k-blocks; the wave's
+        // LDS operations complete in order, so a slot's next writes land
+        // after its reads
+        u32x4 wf[NB][DSPAN];
+        auto transpose = [&](const u32x4(&raw)[4], u32x4(&fr)[DSPAN]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < DSPLIT_BATCH; ++i)
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * j + lr;
+                slot[r * 16 + (lu ^ r)] = raw[j];
+            }
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int kb = 0; kb < DSPAN; ++kb) fr[kb] = slot[orow * 16 + ((4 * kb + ochunk) ^ orow)];
+        };
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[b][mt], wf[i][b], xf[i][mt]);
+        for (int g = 0; g < NB; ++g) {
+            transpose(rw[g], wf[g]);
+            // the blocks groups 0..g complete: (g, mt <= g) and (b < g, g)
+#pragma unroll
+            for (int kb = 0; kb < DSPAN; ++kb) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (mt <= g) mma_chunk<DT>(acc[g][mt], wf[g][kb], xf[mt][kb]);
+                if (g < MT) {
+#pragma unroll
+                    for (int b = 0; b < g; ++b) mma_chunk<DT>(acc[b][g], wf[b][kb], xf[g][kb]);
+                }
+            }
+        }
+    }
+    // the last 1..3 k-blocks (a slice that is not whole spans): fragments
+    // loaded straight in operand layout
+    for (; kbs < kb1; ++kbs) {
+        u32x4 wf[NB], xf[MT];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            wf[b] = load16(wtile + ((int64_t)(16 * b + orow) * p.ldw + kbs * 32 + 8 * ochunk) * 2);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            xf[mt] = load16((const char*)p.X +
+                            ((int64_t)min(16 * mt + orow, p.M - 1) * p.ldx + kbs * 32 + 8 * ochunk) * 2);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[b][mt], wf[b], xf[mt]);
     }
     // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each block
 #pragma unroll
@@ -223,15 +293,31 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
             for (int e = 0; e < 4; ++e)
                 part[wave][b][mt][(4 * (lane >> 4) + e) * DPAD + (lane & 15)] = acc[b][mt][e];
     __syncthreads();
-    // the slice's partial (m, n0 + j), t = 64 m + j: 64 consecutive columns per row
-    float* ws = p.ws + (int64_t)ks * p.M * p.N;
-    for (int t = tid; t < DSPLIT_ROWS * p.M; t += DECODE_WAVES * 64) {
-        const int m = t / DSPLIT_ROWS, j = t % DSPLIT_ROWS;
-        const int b = j >> 4, nl = j & 15, mt = m >> 4, ml = m & 15;
-        float sum = 0.0f;
+    unsigned long long t_loop = 0;
+    if (p.rec && tid == 0) t_loop = __builtin_amdgcn_s_memrealtime();
+
+    // the slice's partial, 4 columns per thread (t = 16 m + q: columns
+    // n0 + 4 q .. + 3 of row m): a wave stores 4 rows x 256 contiguous bytes
+    float* ws = p.ws + (int64_t)ks * p.M * p.N + n0;
+    for (int t = tid; t < 16 * p.M; t += DECODE_WAVES * 64) {
+        const int m = t >> 4, q = t & 15;
+        const int b = q >> 2, mt = m >> 4, ml = m & 15;
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < DECODE_WAVES; ++w) sum += part[w][b][mt][nl * DPAD + ml];
-        ws[(int64_t)m * p.N + n0 + j] = sum;
+        for (int w = 0; w < DECODE_WAVES; ++w)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sum[c] += part[w][b][mt][(4 * (q & 3) + c) * DPAD + ml];
+        *(f32x4*)(ws + (int64_t)m * p.N + 4 * q) = sum;
+    }
+    if (p.rec && tid == 0) {
+        // per workgroup: start, loads of the first whole span landed in
+        // wave 0, loads and MFMAs of all waves done, partial issued (100 MHz
+        // real-time counter)
+        unsigned long long* r = p.rec + 4 * (int64_t)blockIdx.x;
+        r[0] = t_start;
+        r[1] = t_land;
+        r[2] = t_loop;
+        r[3] = __builtin_amdgcn_s_memrealtime();
     }
 }
 

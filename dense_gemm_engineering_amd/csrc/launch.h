@@ -65,8 +65,9 @@ hipError_t skinny_init();
 // Decode-shaped kernel: 1 <= M <= 64, N x K 16-bit weight, one workgroup per
 // 16 weight rows.
 hipError_t launch_decode(int dt, const DecodeArgs& a, hipStream_t s);
-// Split schedule: 17 <= M <= 64, N % 64 == 0, K % 32 == 0; a.ws holds
-// a.ksplit x M x N fp32 partials (the split-K fixup finishes C).
+// Split schedule: 17 <= M <= 64, N % 64 == 0, K % 32 == 0, every wave of a
+// slice with at least one k-block; a.ws receives a.ksplit x M x N fp32
+// partials (the split-K fixup finishes C).
 hipError_t launch_decode_split(int dt, const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_naive(int dt, const SimpleArgs& a, hipStream_t s);

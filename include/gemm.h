@@ -130,7 +130,7 @@ typedef enum {
                                  problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO uses it
                                  whenever eligible ("Matrix Multiplication: The
                                  Operation Behind Modern AI", "The shape a language
-                                 model actually runs").  For 33 <= M <= 64 with
+                                 model actually runs").  For 17 <= M <= 64 with
                                  N % 64 == 0 and K % 32 == 0 it also splits K over
                                  workgroups (64 weight rows each, X read once per
                                  workgroup) when the workspace holds the fp32

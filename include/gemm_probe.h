@@ -41,6 +41,24 @@ gemm_status_t gemm_probe_clock(gemm_in_t in_type, int64_t M, int64_t N, int64_t 
                                gemm_epilogue_t epi, const void* bias, unsigned long long* clk,
                                int64_t clk_entries, void* stream);
 
+/* Phase records of the schedules whose time is not in their MFMA work:
+ * C = A B (trans_b = 0) or A B^T (trans_b = 1) with the epilogue `epi`
+ * (alpha = 1, beta = 0), run as gemm_ex runs it with this workspace, plus 4
+ * unsigned 64-bit values of the 100 MHz real-time counter per workgroup at
+ * rec[4 w .. 4 w + 3].  Supported: the split decode schedule (M <= 64 rows
+ * against an N x K weight with a workspace of gemm_workspace_size bytes;
+ * the records cover its first kernel, the fixup that follows has none):
+ * start, the first 128-deep span's loads landed in wave 0, loads and MFMAs
+ * of all 8 waves done, partial issued.  Other schedules return GEMM_ERR_NOT_SUPPORTED and enqueue nothing,
+ * as does a grid of more than rec_entries workgroups.  rec must be 16-byte
+ * aligned; C receives the same result as gemm_ex. */
+gemm_status_t gemm_probe_phases(gemm_in_t in_type, int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                int trans_b, void* C, int64_t ldc, gemm_out_t c_type,
+                                gemm_epilogue_t epi, const void* bias, void* workspace,
+                                size_t workspace_bytes, unsigned long long* rec,
+                                int64_t rec_entries, void* stream);
+
 /* Matrix work of the 8-wave 256 x 256 GEMM tile without its loads, LDS
  * traffic or stores: GEMM_PROBE_MFMA_GRID workgroups; each of their 8 waves
  * reads two 32-deep k-blocks of fp16 (in_type GEMM_IN_F16) or bf16

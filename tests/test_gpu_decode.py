@@ -86,10 +86,12 @@ def _split_ws(M, N, K, dtype):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(33, 64, 4096), (32, 4096, 4096), (48, 1088, 11008),
-                                   (64, 4096, 4096), (64, 128, 8192), (40, 192, 256)])
+                                   (64, 4096, 4096), (64, 128, 8192), (40, 192, 256),
+                                   (17, 256, 4096), (24, 4096, 1056)])
 def test_decode_split_integer_exact_and_deterministic(M, N, K, dtype):
-    # with a workspace, 33 <= M <= 64 splits K over workgroups of 64 weight
-    # rows (uneven slices at K = 11008); the fp32 partials are summed in slice
+    # with a workspace, 17 <= M <= 64 splits K over workgroups of 64 weight
+    # rows (uneven slices at K = 11008; at K = 1056 every wave has a single
+    # k-block, below a whole 4-block span); the fp32 partials are summed in slice
     # order, so integer inputs give the oracle's bits on every run
     X, W = _ints((M, K), dtype, 6400 + M), _ints((N, K), dtype, 6500 + N)
     T, _ = oracle.gemm(X, W, dtype, trans_b=True, want_U=False)
@@ -102,6 +104,33 @@ def test_decode_split_integer_exact_and_deterministic(M, N, K, dtype):
         assert_bits(C, T, what="%dx%dx%d %s" % (M, N, K, dtype))
         outs.append(C.cpu())
     assert torch.equal(outs[0], outs[1])
+
+
+def test_decode_split_any_workspace_contents():
+    # the split schedule overwrites its whole partial area before reading
+    # it: a workspace full of arbitrary bits, or just used by a split-K GEMM
+    # and by a decode of another shape, gives the same bits
+    M, N, K = 64, 1024, 4096
+    X, W = _ints((M, K), "f16", 6700), _ints((N, K), "f16", 6701)
+    T, _ = oracle.gemm(X, W, "f16", trans_b=True, want_U=False)
+    nbytes = max(dge.gemm_workspace_size(M, N, K, torch.float16),
+                 dge.gemm_workspace_size_splits(256, 512, 4), 1 << 20)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(6702)
+    ws.view(torch.int32).copy_(torch.randint(-2**31, 2**31 - 1, (ws.numel(),), generator=g,
+                                             dtype=torch.int32))
+    dX, dW = to_dev(X, "f16"), to_dev(W, "f16")
+    for step in range(3):
+        C = dge.gemm_ex(dX, dW, trans_b=True, out_dtype=torch.float32, algo="decode",
+                        workspace=ws)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what="step %d" % step)
+        # other users of the same workspace between the calls
+        A2 = torch.ones((256, 4096), dtype=torch.float16, device="cuda")
+        B2 = torch.ones((4096, 512), dtype=torch.float16, device="cuda")
+        dge.gemm_ex(A2, B2, workspace=ws, algo="mfma", splits=4)
+        dge.gemm_ex(dX[:40], dW[:192], trans_b=True, algo="decode", workspace=ws)
+        torch.cuda.synchronize()
 
 
 def test_decode_split_epilogue():

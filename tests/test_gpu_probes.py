@@ -7,6 +7,8 @@
   operands every lane's sum is exact in fp32 and equals the same sum of
   products computed with integers on the host (the lane -> row / column map
   of a 16x16x32 block with swapped operands).
+* gemm_probe_phases gives the same bits as the split decode schedule it
+  instruments and ordered phase records, one set per workgroup.
 * the streaming probes read / copy every byte.
 """
 import numpy as np
@@ -18,6 +20,34 @@ from dense_gemm_engineering_amd import inputs
 from gpu_util import bits_of, to_dev
 
 pytestmark = pytest.mark.gpu
+
+
+def test_probe_phases_split_decode():
+    M, N, K = 64, 4096, 4096
+    X, W = inputs.decode_shape(M)
+    dX, dW = to_dev(X, "f16"), to_dev(W, "f16")
+    ws = torch.empty(dge.gemm_workspace_size(M, N, K, torch.float16) // 4, dtype=torch.float32,
+                     device="cuda")
+    C0 = dge.gemm_f16(dX, dW, trans_b=True, workspace=ws)
+    C1 = torch.empty_like(C0)
+    rec = torch.zeros(4 * 300, dtype=torch.int64, device="cuda")
+    dge.probe_phases(dX, dW, C1, rec, trans_b=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(C0), bits_of(C1))
+    r = rec.view(-1, 4).cpu().numpy()
+    nwg = N // 64 * 4  # 4 K slices of 64 weight rows
+    assert np.all(r[nwg:] == 0)
+    r = r[:nwg].astype(np.float64)
+    assert np.all(np.diff(r, axis=1) >= 0), "phases out of order"
+    span_us = (r[:, 3].max() - r[:, 0].min()) / 100.0
+    assert 0.5 < span_us < 1000.0, span_us
+    # a grid larger than the records, and a schedule without phase records
+    with pytest.raises(dge.GemmError) as e:
+        dge.probe_phases(dX, dW, C1, rec[:4 * (nwg - 1)], trans_b=True, workspace=ws)
+    assert e.value.status == 2
+    with pytest.raises(dge.GemmError) as e:
+        dge.probe_phases(dX, dW, C1, rec, trans_b=True)  # no workspace: one-pass kernel
+    assert e.value.status == 2
 
 
 def test_probe_clock_same_bits_and_sane_clock():
