@@ -588,7 +588,12 @@ bool skinny_eligible(const Gemm& g) {
     if (g.dt == IN_F32 || g.K < 32 || g.K > 256 || g.K % 32 != 0 || g.N > 256) return false;
     if (!aligned16(g.A) || g.lda % 8 != 0) return false;
     const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
-    return skinny_lds_bytes(nt, (int)g.K + 8, out_bytes(g.c_type), 2) <= 160 * 1024;
+    return skinny_lds_bytes(g.trans_b, nt, (int)g.K, out_bytes(g.c_type), 2) <= 160 * 1024;
+}
+
+// The automatic schedule takes the tall-skinny kernel for M >> N.
+bool skinny_auto(const Gemm& g) {
+    return skinny_eligible(g) && g.M >= 8 * g.N && g.M >= 4096 && env_int("GEMM_SKINNY", 1) != 0;
 }
 
 gemm_status_t run_skinny(const Gemm& g, int cus) {
@@ -602,18 +607,20 @@ gemm_status_t run_skinny(const Gemm& g, int cus) {
     a.M = (int)g.M;
     a.N = (int)g.N;
     a.K = (int)g.K;
-    a.pitch = (int)g.K + 8;
+    const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
+    a.pitch = skinny_pitch(g.trans_b, (int)g.K);
     a.c_type = g.c_type;
     const int cb = out_bytes(g.c_type);
     a.vec_c = (aligned16(g.B) && g.ldb % 8 == 0 ? 2 : 0) |
               (aligned16(g.C) && (g.ldc * cb) % 16 == 0 && (g.N * cb) % 16 == 0 ? 4 : 0);
     a.ep = make_epilogue(g);
-    const int nt = (ceil_div(g.N, 16) + 1) / 2 * 2;
-    const int waves = skinny_waves(nt, a.pitch, cb);
-    const size_t lds = skinny_lds_bytes(nt, a.pitch, cb, waves);
+    a.rec = g.clk;
+    const int waves = skinny_waves(g.trans_b, nt, (int)g.K, cb);
+    const size_t lds = skinny_lds_bytes(g.trans_b, nt, (int)g.K, cb, waves);
     // one workgroup per CU: W is staged once per CU and amortised over the
     // CU's share of the rows (16 * skinny_rb per wave per step)
     const int grid = std::max(1, std::min(ceil_div(g.M, waves * 16 * skinny_rb(nt)), cus));
+    if (g.clk && g.clk_cap < grid) return GEMM_ERR_NOT_SUPPORTED;
     return launch_status(launch_skinny(g.dt, nt, g.trans_b, a, grid, waves, lds, g.stream));
 }
 
@@ -710,8 +717,7 @@ gemm_status_t run_gemm(const Gemm& g, const gemm_tuning_t* tuning) {
         case GEMM_ALGO_AUTO:
             if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && g.K > 0 && decode_eligible(g))
                 return run_decode(g, dev.cus);
-            if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && skinny_eligible(g) &&
-                g.M >= 8 * g.N && g.M >= 4096 && env_int("GEMM_SKINNY", 1) != 0)
+            if (tn.tile == GEMM_TILE_AUTO && tn.splits <= 1 && skinny_auto(g))
                 return run_skinny(g, dev.cus);
             return run_mfma(g, tn.tile, tn.splits, dev.cus, 1);
         default:
@@ -845,6 +851,7 @@ gemm_status_t gemm_probe_phases(gemm_in_t in_type, int64_t M, int64_t N, int64_t
     DeviceInfo dev;
     if ((st = current_device(&dev)) != GEMM_OK) return st;
     if (decode_eligible(g) && decode_ksplit(g.M, g.N, g.K, dev.cus) > 1) return run_decode(g, dev.cus);
+    if (skinny_auto(g)) return run_skinny(g, dev.cus);
     return GEMM_ERR_NOT_SUPPORTED;
 }
 

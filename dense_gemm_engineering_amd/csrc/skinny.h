@@ -5,11 +5,18 @@
 // streaming X:
 //
 //  * One workgroup per CU with 8 waves.  W sits in LDS once per workgroup
-//    for the whole kernel, stored transposed ([n][k], k-contiguous, rows
-//    padded by 16 bytes) so that it can serve as the MFMA "A" operand of
-//    C^T = W^T X^T; the bias is staged next to it as fp32.  A wave reads all
-//    the W^T fragments of a 32-deep k-block at once (so their LDS latencies
-//    overlap) and, up to N = 64, applies each to two 16-row blocks.
+//    for the whole kernel and serves as the MFMA "A" operand of C^T = W^T
+//    X^T; the bias is staged next to it as fp32.  An N x K W is stored as it
+//    is ([n][k], rows padded by 16 bytes) and its fragments are plain
+//    16-byte reads.  A K x N W is also stored as it is ([k][n] in blocks of
+//    64 columns, 16-byte chunks XOR-swizzled by k-row) and its W^T
+//    fragments are read with ds_read_b64_tr_b16, as the GEMM reads a K x N
+//    B: its loads are then whole rows of W, 16 bytes per lane, and its LDS
+//    writes plain 16-byte stores.  (Transposing on the way in instead needs
+//    each lane on a pair of k-rows, so that every load of a wave touched 64
+//    cache lines: staging 51 KB took ~3 us at N = K = 160.)  A wave reads
+//    all the W^T fragments of a 32-deep k-block at once (so their LDS
+//    latencies overlap) and, up to N = 64, applies each to two 16-row blocks.
 //  * X needs no LDS: the MFMA "B" operand of X^T is 8 consecutive k of one
 //    row of X per lane, i.e. a 16-byte load straight from memory into the
 //    operand registers.  Each wave owns 16 rows (32 for N <= 64) at a time
@@ -34,11 +41,14 @@ struct SkinnyArgs {
     void* C;
     int64_t ldx, ldw, ldc;
     int M, N, K;
-    int pitch;   // LDS row pitch of W^T in elements (K + 8)
+    int pitch;   // LDS row pitch of W in elements (skinny_pitch)
     int c_type;
     int vec_c;   // bit 1: W rows allow aligned 16-byte loads; bit 2: C rows are
                  // 16-byte aligned and N fills whole 16-byte chunks
     Epilogue ep;
+    // phase records (may be null): 4 real-time counter values per workgroup,
+    // taken by its first thread
+    unsigned long long* rec;
 };
 
 constexpr int SKINNY_KBMAX = 8;        // K <= 256
@@ -53,20 +63,50 @@ __host__ __device__ constexpr int skinny_kch(int) { return 8; }
 // Waves per workgroup at most (256 registers per lane).
 __host__ __device__ constexpr int skinny_max_waves(int) { return 8; }
 
-// Dynamic LDS: W^T (NT*16 rows x pitch halves), the bias (NT*16 fp32), then
-// one output staging tile per wave (RB*16 rows x (NT*16*out_bytes + 16) bytes).
+// A K x N W sits in LDS in column blocks of SKINNY_CB = 64 columns, each K
+// rows of 128 bytes (8 chunks of 16 bytes), as many blocks as NT*16 columns
+// need.  With the fixed 128-byte row every k-row offset a k-block's fragment
+// reads need stays well below 64 KB, an immediate of the read.
+constexpr int SKINNY_CB = 64;
+__host__ __device__ constexpr int skinny_cblocks(int nt) { return (nt * 16 + SKINNY_CB - 1) / SKINNY_CB; }
+// LDS row pitch in elements: K + 8 for an N x K W ([n][k]), SKINNY_CB for a
+// K x N W ([block][k][n % 64])
+__host__ __device__ inline int skinny_pitch(int trans_b, int K) {
+    return trans_b ? K + 8 : SKINNY_CB;
+}
+__host__ __device__ inline size_t skinny_w_bytes(int trans_b, int nt, int K) {
+    return trans_b ? (size_t)nt * 16 * (K + 8) * 2 : (size_t)skinny_cblocks(nt) * K * SKINNY_CB * 2;
+}
+// Dynamic LDS: W, the bias (NT*16 fp32), then one output staging tile per
+// wave (RB*16 rows x (NT*16*out_bytes + 16) bytes).
 __host__ __device__ inline size_t skinny_stage_bytes(int nt, int out_bytes) {
     return (size_t)16 * skinny_rb(nt) * (nt * 16 * out_bytes + 16);
 }
-__host__ __device__ inline size_t skinny_lds_bytes(int nt, int pitch, int out_bytes, int waves) {
-    return (size_t)nt * 16 * pitch * 2 + (size_t)nt * 16 * 4 +
+__host__ __device__ inline size_t skinny_lds_bytes(int trans_b, int nt, int K, int out_bytes,
+                                                   int waves) {
+    return skinny_w_bytes(trans_b, nt, K) + (size_t)nt * 16 * 4 +
            (size_t)waves * skinny_stage_bytes(nt, out_bytes);
 }
 // Waves per workgroup: the most (8, 4, 2 or 1) whose staging fits 160 KB.
-inline int skinny_waves(int nt, int pitch, int out_bytes) {
+inline int skinny_waves(int trans_b, int nt, int K, int out_bytes) {
     int w = skinny_max_waves(nt);
-    while (w > 1 && skinny_lds_bytes(nt, pitch, out_bytes, w) > 160 * 1024) w /= 2;
+    while (w > 1 && skinny_lds_bytes(trans_b, nt, K, out_bytes, w) > 160 * 1024) w /= 2;
     return w;
+}
+// XOR swizzle of the 16-byte chunks of k-row k of a K x N W (8 chunks a
+// row): a transposed fragment read covers 16 k-rows (k % 4 = 0..3 from each
+// of the 4 lane groups, 8 apart) x 32 bytes.  With 128-byte rows, k-rows of
+// one parity share bank groups unless bit 1 of k moves them, and lane
+// groups 0 / 1 (and 2 / 3) unless bit 3 does: the 32-byte pair index is
+// XORed with those two bits, so each half of the read (32 lanes) covers 8
+// different 32-byte bank groups.
+__device__ inline int swz_kn(int k) { return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2); }
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ inline uint2 skinny_read_tr(const lds_u16* p) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)p);
+    return __builtin_bit_cast(uint2, v);
 }
 
 template <int OT>
@@ -82,13 +122,14 @@ __device__ inline void skinny_load4(const SkinnyArgs& p, int m, int n0, float* t
 // rounded values staged in the wave's LDS tile (rows of pitch_o bytes), then
 // written out row by row with 16-byte non-temporal stores so that a wave writes whole
 // rows of C.
-template <int OT, int NT, int RB>
+// The epilogue kind is a template argument (EPI): with it a runtime flag,
+// the compiler evaluated bias and GELU for every output and selected.
+template <int OT, int NT, int RB, int EPI>
 __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB][NT],
                                      const float* bias_s, int base, int lane, char* stage) {
     typedef typename OutType<OT>::T T;
     constexpr int OB = OutType<OT>::BYTES;
     constexpr int pitch_o = NT * 16 * OB + 16;
-    const bool has_bias = p.ep.epi != EPI_NONE, gelu = p.ep.epi == EPI_BIAS_GELU;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int ml = rb * 16 + (lane & 15);
@@ -96,16 +137,21 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB]
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n0 = nt * 16 + 4 * (lane >> 4);
-            float old[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.ep.beta != 0.0f && m < p.M && n0 < p.N) skinny_load4<OT>(p, m, n0, old);
-            const f32x4 b = *(const f32x4*)(bias_s + n0);  // zero past N
+            f32x4 b = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI != EPI_NONE) b = *(const f32x4*)(bias_s + n0);  // zero past N
             float t[4];
+            if (p.ep.beta != 0.0f) {  // wave-uniform; a branch around loads of C
+                float old[4] = {0.f, 0.f, 0.f, 0.f};
+                if (m < p.M && n0 < p.N) skinny_load4<OT>(p, m, n0, old);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = p.ep.alpha * acc[rb][nt][e];
-                if (p.ep.beta != 0.0f) v += p.ep.beta * old[e];
-                if (has_bias) v += b[e];
-                t[e] = gelu ? gelu_tanh(v) : v;
+                for (int e = 0; e < 4; ++e) t[e] = p.ep.alpha * acc[rb][nt][e] + p.ep.beta * old[e] + b[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf(p.ep.alpha, acc[rb][nt][e], b[e]);
+            }
+            if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = gelu_tanh(t[e]);
             }
             char* dst = stage + ml * pitch_o + n0 * OB;
             if constexpr (OB == 2) {
@@ -150,23 +196,33 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB]
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 }
 
-// W^T into LDS ([n][k], rows n >= N zero-filled), by nth threads, one batch
-// (BT tasks per thread) at a time: load() brings a batch into registers,
-// store() writes it to LDS, so that other loads can be issued in between.
-// N x K W: a task is 8 consecutive k of one n, stored as one 16-byte LDS
-// write.  K x N W: a task is a pair of k-rows x 8 consecutive n (two 16-byte
-// loads), stored as eight 32-bit LDS writes of (k, k+1) pairs; consecutive
-// lanes take consecutive k-pairs, so the transposing writes of a wave fall
-// in consecutive dwords (a one-element-per-lane transpose put every lane of
-// a wave on the same bank).
+template <int NT, int RB, int EPI>
+__device__ inline void skinny_finish_ot(const SkinnyArgs& p, const f32x4 (&acc)[RB][NT],
+                                        const float* bias_s, int base, int lane, char* stage) {
+    if (p.c_type == OUT_F16)
+        skinny_finish<OUT_F16, NT, RB, EPI>(p, acc, bias_s, base, lane, stage);
+    else if (p.c_type == OUT_BF16)
+        skinny_finish<OUT_BF16, NT, RB, EPI>(p, acc, bias_s, base, lane, stage);
+    else
+        skinny_finish<OUT_F32, NT, RB, EPI>(p, acc, bias_s, base, lane, stage);
+}
+
+// W into LDS by nth threads, one batch (BT tasks per thread) at a time:
+// load() brings a batch into registers, store() writes it to LDS, so that
+// other loads can be issued in between.  A task is one 16-byte chunk: 8
+// consecutive k of one n-row of an N x K W, or 8 consecutive n of one k-row
+// of a K x N W (chunks past N zero-filled up to NT*16 columns); consecutive
+// lanes take consecutive chunks of a row, so the loads of a wave cover
+// whole rows.
 template <int DT, int NT, bool TRANS_B>
 struct WStage {
     static constexpr int NP = NT * 16;
-    static constexpr int BT = TRANS_B ? 8 : 4;  // tasks per thread per batch: one batch at N = K = 160
-    u32x4 v0[BT], v1[BT];
+    static constexpr int BT = 8;  // tasks per thread per batch: one batch at N = K = 160
+    u32x4 v[BT];
 
+    __device__ static inline int per_row(const SkinnyArgs& p) { return TRANS_B ? p.K / 8 : NP / 8; }
     __device__ static inline int ntask(const SkinnyArgs& p) {
-        return TRANS_B ? NP * (p.K / 8) : (p.K / 2) * (NP / 8);
+        return TRANS_B ? NP * (p.K / 8) : p.K * (NP / 8);
     }
     // Task t of this workgroup is task (t + rot) mod ntask: every workgroup
     // wants all of W at the same moment, and rotating the order spreads the
@@ -177,62 +233,48 @@ struct WStage {
     }
     __device__ inline void load(const SkinnyArgs& p, int t0, int tid, int nth, int rot) {
         const bool vec_w = (p.vec_c & 2) != 0;  // W rows allow aligned 16-byte loads
-        const int nt_all = ntask(p);
+        const int nt_all = ntask(p), pr = per_row(p);
 #pragma unroll
         for (int i = 0; i < BT; ++i) {
             const int tt = t0 + i * nth + tid;
-            v0[i] = v1[i] = (u32x4){0, 0, 0, 0};
+            v[i] = (u32x4){0, 0, 0, 0};
             if (tt >= nt_all) continue;
             const int t = rotated(tt, rot, nt_all);
+            const int row = t / pr, c8 = (t - row * pr) * 8;
             if constexpr (TRANS_B) {
-                const int per_line = p.K / 8;
-                const int n = t / per_line, k8 = (t - n * per_line) * 8;
-                if (n >= p.N) continue;
-                const int64_t idx = (int64_t)n * p.ldw + k8;
-                v0[i] = vec_w ? load16((const char*)p.W + idx * 2) : load_chunk_masked<DT>(p.W, idx, 8);
+                if (row >= p.N) continue;
+                const int64_t idx = (int64_t)row * p.ldw + c8;
+                v[i] = vec_w ? load16((const char*)p.W + idx * 2) : load_chunk_masked<DT>(p.W, idx, 8);
             } else {
-                const int kp_count = p.K / 2;
-                const int n8 = (t / kp_count) * 8, kp = t - (t / kp_count) * kp_count;
-                if (n8 >= p.N) continue;
-                const int64_t i0 = (int64_t)(2 * kp) * p.ldw + n8, i1 = i0 + p.ldw;
-                if (vec_w && n8 + 8 <= p.N) {
-                    v0[i] = load16((const char*)p.W + i0 * 2);
-                    v1[i] = load16((const char*)p.W + i1 * 2);
-                } else {
-                    v0[i] = load_chunk_masked<DT>(p.W, i0, p.N - n8);
-                    v1[i] = load_chunk_masked<DT>(p.W, i1, p.N - n8);
-                }
+                if (c8 >= p.N) continue;
+                const int64_t idx = (int64_t)row * p.ldw + c8;
+                v[i] = vec_w && c8 + 8 <= p.N ? load16((const char*)p.W + idx * 2)
+                                              : load_chunk_masked<DT>(p.W, idx, p.N - c8);
             }
         }
     }
     __device__ inline void store(const SkinnyArgs& p, uint16_t* wt, int t0, int tid, int nth,
                                  int rot) const {
-        const int nt_all = ntask(p);
+        const int nt_all = ntask(p), pr = per_row(p);
 #pragma unroll
         for (int i = 0; i < BT; ++i) {
             const int tt = t0 + i * nth + tid;
             if (tt >= nt_all) continue;
             const int t = rotated(tt, rot, nt_all);
-            if constexpr (TRANS_B) {
-                const int per_line = p.K / 8;
-                const int n = t / per_line, k8 = (t - n * per_line) * 8;
-                *(u32x4*)(wt + n * p.pitch + k8) = v0[i];
-            } else {
-                const int kp_count = p.K / 2;
-                const int n8 = (t / kp_count) * 8, kp = t - (t / kp_count) * kp_count;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t lo = (v0[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    const uint32_t hi = (v1[i][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    *(uint32_t*)(wt + (n8 + e) * p.pitch + 2 * kp) = lo | (hi << 16);
-                }
-            }
+            const int row = t / pr, c = t - row * pr;
+            if constexpr (TRANS_B)
+                *(u32x4*)(wt + row * p.pitch + 8 * c) = v[i];
+            else
+                *(u32x4*)(wt + (c >> 3) * p.K * SKINNY_CB + row * SKINNY_CB +
+                          8 * ((c & 7) ^ swz_kn(row))) = v[i];
         }
     }
 };
 
 // The X operand registers of k-blocks kb0 .. kb0 + KCH - 1 of one wave's
-// RB x 16 rows starting at row base.
+// RB x 16 rows starting at row base.  (Loading whole rows and moving them
+// into operand layout through LDS, as the decode kernel does for its
+// weight, measured slower here: 14.6 -> 16.8 us at N = K = 160.)
 template <int RB, int KCH>
 __device__ inline void skinny_load_x(const SkinnyArgs& p, int base, int kb0, int lane,
                                      u32x4 (&xf)[RB][KCH]) {
@@ -258,6 +300,9 @@ __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(
     const int KB = p.K / 32;
     const int rows_per_step = nwaves * RB * 16 * gridDim.x;
     int base = (blockIdx.x * nwaves + wave) * RB * 16;
+    const bool rec = p.rec && tid == 0;
+    unsigned long long t_start = 0, t_w = 0, t_x = 0;
+    if (rec) t_start = __builtin_amdgcn_s_memrealtime();
 
     // Prologue: W and the bias are staged before any X is requested (issued
     // together, X would flood the memory system and W, which every wave
@@ -282,16 +327,39 @@ __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(
         wst.load(p, t0, tid, nth, rot);
         wst.store(p, wt, t0, tid, nth, rot);
     }
-    float* bias_s = (float*)(wt + NT * 16 * p.pitch);
+    float* bias_s = (float*)((char*)wt + skinny_w_bytes(TRANS_B, NT, p.K));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         if (tid + i * nth < NT * 16) bias_s[tid + i * nth] = InType<DT>::to_f32(bias_bits[i]);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
     __builtin_amdgcn_s_barrier();
+    if (rec) t_w = __builtin_amdgcn_s_memrealtime();
     u32x4 xf[RB][KCH];
     if (base < p.M) skinny_load_x<RB, KCH>(p, base, 0, lane, xf);
+    if (rec) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first rows have landed
+        t_x = __builtin_amdgcn_s_memrealtime();
+    }
 
     const uint16_t* wrow = wt + (lane & 15) * p.pitch + 8 * (lane >> 4);
+    // K x N W: transposed fragment reads.  Lane group g = lane / 16 covers
+    // k-rows 32 kb + 8 g + 4 h + t / 4 (t = lane % 16) and columns 16 nt +
+    // 4 (t % 4); lane t receives column 16 nt + t, 4 k per read, 8 for the
+    // two halves h.  The k-row's swizzle depends only on t / 4 and g % 2
+    // (k % 4 and bit 3 of k), so each lane's offsets within a k-block are
+    // fixed: tr_off[nt] elements past the k-block's uniform row.
+    const lds_u16* wt3 = (const lds_u16*)wt;
+    int tr_off[TRANS_B ? 1 : NT];
+    if constexpr (!TRANS_B) {
+        const int t = lane & 15, g = lane >> 4;
+        const int sw = (((t >> 3) & 1) << 1) | ((g & 1) << 2);  // swz_kn of those k-rows
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = nt * 16 + 4 * (t & 3), nb = n % SKINNY_CB;
+            tr_off[nt] = (n / SKINNY_CB) * p.K * SKINNY_CB + (8 * g + (t >> 2)) * SKINNY_CB +
+                         8 * ((nb >> 3) ^ sw) + (n & 7);
+        }
+    }
     const int ob = p.c_type == OUT_F32 ? 4 : 2;
     char* stage = (char*)(bias_s + NT * 16) + wave * skinny_stage_bytes(NT, ob);
     for (; base < p.M; base += rows_per_step) {
@@ -303,29 +371,56 @@ __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(
 #pragma unroll
         for (int c0 = 0; c0 < SKINNY_KBMAX; c0 += KCH) {
             if (c0 >= KB) break;
-            if (c0 > 0) skinny_load_x<RB, KCH>(p, base, c0, lane, xf);
 #pragma unroll
             for (int kb = 0; kb < KCH; ++kb) {
                 if (c0 + kb >= KB) break;
                 // all of this k-block's W^T fragments first, then the MFMAs
                 u32x4 wf[NT];
+                if constexpr (TRANS_B) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    wf[nt] = *(const u32x4*)(wrow + nt * 16 * p.pitch + (c0 + kb) * 32);
+                    for (int nt = 0; nt < NT; ++nt)
+                        wf[nt] = *(const u32x4*)(wrow + nt * 16 * p.pitch + (c0 + kb) * 32);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        // uniform, and with the fixed row pitch an immediate
+                        // offset (a runtime pitch made the compiler hold an
+                        // address per (k-block, h, nt) across steps)
+                        const lds_u16* kp = wt3 + ((c0 + kb) * 32 + 4 * h) * SKINNY_CB;
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const uint2 v = skinny_read_tr(kp + tr_off[nt]);
+                            wf[nt][2 * h] = v.x;
+                            wf[nt][2 * h + 1] = v.y;
+                        }
+                    }
+                }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) mma_chunk<DT>(acc[rb][nt], wf[nt], xf[rb][kb]);
+                // keep the next k-block's fragment reads after these MFMAs
+                // (hoisted, they hold NT more registers per k-block)
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // the next rows' loads overlap this epilogue's stores
         if (base + rows_per_step < p.M) skinny_load_x<RB, KCH>(p, base + rows_per_step, 0, lane, xf);
-        if (p.c_type == OUT_F16)
-            skinny_finish<OUT_F16, NT, RB>(p, acc, bias_s, base, lane, stage);
-        else if (p.c_type == OUT_BF16)
-            skinny_finish<OUT_BF16, NT, RB>(p, acc, bias_s, base, lane, stage);
+        if (p.ep.epi == EPI_BIAS_GELU)
+            skinny_finish_ot<NT, RB, EPI_BIAS_GELU>(p, acc, bias_s, base, lane, stage);
+        else if (p.ep.epi == EPI_BIAS)
+            skinny_finish_ot<NT, RB, EPI_BIAS>(p, acc, bias_s, base, lane, stage);
         else
-            skinny_finish<OUT_F32, NT, RB>(p, acc, bias_s, base, lane, stage);
+            skinny_finish_ot<NT, RB, EPI_NONE>(p, acc, bias_s, base, lane, stage);
+    }
+    if (rec) {
+        // start, W staged (barrier passed), wave 0's first rows landed, wave 0's
+        // last stores issued
+        unsigned long long* r = p.rec + 4 * (int64_t)blockIdx.x;
+        r[0] = t_start;
+        r[1] = t_w;
+        r[2] = t_x;
+        r[3] = __builtin_amdgcn_s_memrealtime();
     }
 }
 

@@ -45,13 +45,17 @@ gemm_status_t gemm_probe_clock(gemm_in_t in_type, int64_t M, int64_t N, int64_t 
  * C = A B (trans_b = 0) or A B^T (trans_b = 1) with the epilogue `epi`
  * (alpha = 1, beta = 0), run as gemm_ex runs it with this workspace, plus 4
  * unsigned 64-bit values of the 100 MHz real-time counter per workgroup at
- * rec[4 w .. 4 w + 3].  Supported: the split decode schedule (M <= 64 rows
- * against an N x K weight with a workspace of gemm_workspace_size bytes;
- * the records cover its first kernel, the fixup that follows has none):
- * start, the first 128-deep span's loads landed in wave 0, loads and MFMAs
- * of all 8 waves done, partial issued.  Other schedules return GEMM_ERR_NOT_SUPPORTED and enqueue nothing,
- * as does a grid of more than rec_entries workgroups.  rec must be 16-byte
- * aligned; C receives the same result as gemm_ex. */
+ * rec[4 w .. 4 w + 3].  Supported schedules and their records:
+ *   - split decode (M <= 64 rows against an N x K weight, a workspace of
+ *     gemm_workspace_size bytes; the records cover its first kernel, not
+ *     the fixup): start, the first 128-deep span's loads landed in wave 0,
+ *     loads and MFMAs of all 8 waves done, partial issued;
+ *   - tall-skinny (M >= 4096, M >= 8 N, N and K <= 256): start, W staged in
+ *     LDS, wave 0's first rows of A landed, wave 0's last stores issued.
+ * Other schedules return GEMM_ERR_NOT_SUPPORTED and enqueue nothing, as does
+ * a grid of more than rec_entries workgroups.  The waits that take the
+ * "landed" records delay wave 0 slightly.  rec must be 16-byte aligned; C
+ * receives the same result as gemm_ex. */
 gemm_status_t gemm_probe_phases(gemm_in_t in_type, int64_t M, int64_t N, int64_t K,
                                 const void* A, int64_t lda, const void* B, int64_t ldb,
                                 int trans_b, void* C, int64_t ldc, gemm_out_t c_type,

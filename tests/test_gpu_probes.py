@@ -7,8 +7,8 @@
   operands every lane's sum is exact in fp32 and equals the same sum of
   products computed with integers on the host (the lane -> row / column map
   of a 16x16x32 block with swapped operands).
-* gemm_probe_phases gives the same bits as the split decode schedule it
-  instruments and ordered phase records, one set per workgroup.
+* gemm_probe_phases gives the same bits as the split decode and tall-skinny
+  schedules it instruments and ordered phase records, one set per workgroup.
 * the streaming probes read / copy every byte.
 """
 import numpy as np
@@ -47,6 +47,26 @@ def test_probe_phases_split_decode():
     assert e.value.status == 2
     with pytest.raises(dge.GemmError) as e:
         dge.probe_phases(dX, dW, C1, rec, trans_b=True)  # no workspace: one-pass kernel
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("N", [160, 32])
+def test_probe_phases_tall_skinny(N):
+    X, W, bias = inputs.tall_skinny(N)
+    dX, dW, db = to_dev(X, "f16"), to_dev(W, "f16"), to_dev(bias, "f16")
+    C0 = dge.gemm_f16(dX, dW, epi="bias_gelu", bias=db)
+    C1 = torch.empty_like(C0)
+    rec = torch.zeros(4 * 300, dtype=torch.int64, device="cuda")
+    dge.probe_phases(dX, dW, C1, rec, epi="bias_gelu", bias=db)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(C0), bits_of(C1))
+    r = rec.view(-1, 4).cpu().numpy()
+    nwg = int((r[:, 0] != 0).sum())
+    assert 1 <= nwg <= 256 and np.all(r[nwg:] == 0)
+    r = r[:nwg].astype(np.float64)
+    assert np.all(np.diff(r, axis=1) >= 0), "phases out of order"
+    with pytest.raises(dge.GemmError) as e:
+        dge.probe_phases(dX, dW, C1, rec[:4 * (nwg - 1)], epi="bias_gelu", bias=db)
     assert e.value.status == 2
 
 
