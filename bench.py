@@ -687,6 +687,68 @@ def _kernel_set_calls(name, dge, inputs, torch):
 KERNEL_SETS = ("square4096", "prefill", "skinny", "decode", "streamk")
 
 
+def run_phases(dge, inputs, torch, steps, repeats=5):
+    """Phase records (gemm_probe_phases: 100 MHz real-time counter, per
+    workgroup) of the split decode at M = 32 and 64 and the tall-skinny
+    bias+GELU at N = 160 and 32.  Each record follows `steps` back-to-back
+    calls of the same shape (HBM-cold weight / input sets, so the clock and
+    caches are in their steady state); per phase the median and maximum over
+    workgroups, relative to the earliest workgroup start, medians over
+    `repeats` records."""
+    out = {}
+
+    def summarize_rec(recs, names):
+        rows = []
+        for r in recs:
+            r = r[r[:, 0] > 0].astype(np.float64)
+            r = (r - r[:, 0].min()) / 100.0
+            rows.append([[float(np.median(r[:, i])), float(r[:, i].max())] for i in range(4)])
+        a = np.median(np.array(rows), axis=0)
+        return {n: {"median_us": round(float(a[i][0]), 3), "max_us": round(float(a[i][1]), 3)}
+                for i, n in enumerate(names)}
+
+    _, W = inputs.decode_shape(1)
+    nset = max(1, int(np.ceil(300e6 / (4096 * 4096 * 2))))
+    Ws = [_dev(W, "f16", torch) for _ in range(nset)]
+    for M in (32, 64):
+        X, _ = inputs.decode_shape(M)
+        dX = _dev(X, "f16", torch)
+        C = torch.empty((M, 4096), dtype=torch.float16, device="cuda")
+        ws = torch.empty(dge.gemm_workspace_size(M, 4096, 4096, torch.float16) // 4 + 1,
+                         dtype=torch.float32, device="cuda")
+        rec = torch.zeros(4 * 512, dtype=torch.int64, device="cuda")
+        recs = []
+        for rep in range(repeats):
+            for i in range(steps):
+                dge.gemm_f16(dX, Ws[i % nset], C, trans_b=True, workspace=ws)
+            rec.zero_()
+            dge.probe_phases(dX, Ws[(steps + rep) % nset], C, rec, trans_b=True, workspace=ws)
+            torch.cuda.synchronize()
+            recs.append(rec.view(-1, 4).cpu().numpy())
+        out["decode_M%d" % M] = summarize_rec(
+            recs, ("start", "first_span_landed_wave0", "loads_and_mfma_done", "partial_issued"))
+    del Ws
+    for N in (160, 32):
+        X, Wk, bias = inputs.tall_skinny(N)
+        nset = max(1, int(np.ceil(300e6 / (65536 * (160 + N) * 2))))
+        Xs = [_dev(X, "f16", torch) for _ in range(nset)]
+        dW, db = _dev(Wk, "f16", torch), _dev(bias, "f16", torch)
+        C = torch.empty((65536, N), dtype=torch.float16, device="cuda")
+        rec = torch.zeros(4 * 512, dtype=torch.int64, device="cuda")
+        recs = []
+        for rep in range(repeats):
+            for i in range(steps):
+                dge.gemm_f16(Xs[i % nset], dW, C, epi="bias_gelu", bias=db)
+            rec.zero_()
+            dge.probe_phases(Xs[(steps + rep) % nset], dW, C, rec, epi="bias_gelu", bias=db)
+            torch.cuda.synchronize()
+            recs.append(rec.view(-1, 4).cpu().numpy())
+        out["skinny_N%d" % N] = summarize_rec(
+            recs, ("start", "w_staged", "first_rows_landed_wave0", "wave0_done"))
+        del Xs
+    return out
+
+
 def run_kernel_set(name, dge, inputs, torch, steps, warmup):
     calls = _kernel_set_calls(name, dge, inputs, torch)
     for label, fn in calls:
@@ -717,6 +779,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only a plain 256 MiB device-to-device copy, 5 times (the reference "
                          "for scaling HBM byte counters)")
+    ap.add_argument("--phases", action="store_true",
+                    help="only the phase records of the split decode and tall-skinny kernels")
     ap.add_argument("--kernel-set", choices=sorted(KERNEL_SETS),
                     help="only launch one workload's kernels --steps times each, after "
                          "--warmup launches, and print their names (for profiler runs)")
@@ -730,6 +794,10 @@ def main():
     import dense_gemm_engineering_amd.binding as dge
     from dense_gemm_engineering_amd import inputs
 
+    if args.phases:
+        dge.gemm_init()
+        print(json.dumps({"phases": run_phases(dge, inputs, torch, max(args.steps, 30))}), flush=True)
+        return
     if args.kernel_set:
         run_kernel_set(args.kernel_set, dge, inputs, torch, args.steps, args.warmup)
         return

@@ -184,9 +184,13 @@ template <int DT, int MT>
 __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(DecodeArgs p) {
     constexpr int NB = DSPLIT_ROWS / 16;  // weight blocks per workgroup
     // partial C^T blocks [wave][nb][mt][16 n x 16 m]; during the main loop
-    // each wave's part holds its transpose slot
-    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][NB][MT][16 * DPAD];
-    static_assert(NB * MT * 16 * DPAD * 4 >= 16 * 16 * 16, "transpose slot fits a wave's part");
+    // each wave's part holds its transpose slot.  Each weight block's MT
+    // blocks are padded so that the weight blocks start 16 banks apart: the
+    // summation's 16 lanes of a row read 4 columns from each of the 4 weight
+    // blocks (unpadded, MT x 16 x 17 floats put them on the same banks).
+    constexpr int BSTRIDE = MT * 16 * DPAD + (16 - (MT * 16 * DPAD) % 64 + 64) % 64;
+    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][NB][BSTRIDE];
+    static_assert(NB * BSTRIDE * 4 >= 16 * 16 * 16, "transpose slot fits a wave's part");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     unsigned long long t_start = 0, t_land = 0;
     if (p.rec && tid == 0) t_start = __builtin_amdgcn_s_memrealtime();
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
     const int kb1 = s0 + (wave + 1) * (s1 - s0) / DECODE_WAVES;
     const int lr = lane >> 4, lu = lane & 15;  // load layout: row within 4, 16-byte unit
     const int orow = lane & 15, ochunk = lane >> 4;  // operand layout: row, 8-element chunk
-    u32x4* slot = (u32x4*)&part[wave][0][0][0];
+    u32x4* slot = (u32x4*)&part[wave][0][0];
 
     f32x4 acc[NB][MT];
 #pragma unroll
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                part[wave][b][mt][(4 * (lane >> 4) + e) * DPAD + (lane & 15)] = acc[b][mt][e];
+                part[wave][b][mt * 16 * DPAD + (4 * (lane >> 4) + e) * DPAD + (lane & 15)] = acc[b][mt][e];
     __syncthreads();
     unsigned long long t_loop = 0;
     if (p.rec && tid == 0) t_loop = __builtin_amdgcn_s_memrealtime();
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
 #pragma unroll
         for (int w = 0; w < DECODE_WAVES; ++w)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) sum[c] += part[w][b][mt][(4 * (q & 3) + c) * DPAD + ml];
+            for (int c = 0; c < 4; ++c) sum[c] += part[w][b][mt * 16 * DPAD + (4 * (q & 3) + c) * DPAD + ml];
         *(f32x4*)(ws + (int64_t)m * p.N + 4 * q) = sum;
     }
     if (p.rec && tid == 0) {
