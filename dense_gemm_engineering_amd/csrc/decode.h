@@ -47,6 +47,9 @@ constexpr int DPAD = 17;  // floats per 16-wide row of a partial block in LDS
 // k-blocks whose loads are issued together: 16 (a 4096-deep K in one round
 // trip per wave) while the registers allow, 8 for M > 32
 __host__ __device__ constexpr int decode_batch(int mt) { return mt <= 2 ? 16 : 8; }
+// k-blocks per coalesced weight-load span: each load instruction then covers
+// 4 whole rows x 256 bytes
+constexpr int DSPAN = 4;
 
 // XT: X goes through the per-wave transpose slot (below); off for M = 1,
 // whose clamped rows make every quad read one address anyway.
@@ -58,6 +61,8 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
     __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][MT][16 * DPAD];
     // each wave's X transpose slot: MT blocks of 16 rows x 4 16-byte chunks
     __shared__ __attribute__((aligned(16))) u32x4 xslot[XT ? DECODE_WAVES : 1][MT][64];
+    // each wave's weight transpose slot: 16 rows x 16 16-byte units
+    __shared__ __attribute__((aligned(16))) u32x4 wslot[DECODE_WAVES][256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * 16;
     const int nkb = (p.K + 31) / 32;
@@ -90,7 +95,70 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     constexpr int DECODE_BATCH = decode_batch(MT);
-    for (int kb = kb0; kb < kb1; kb += DECODE_BATCH) {
+    // the k-block's MFMAs on one weight fragment and the batch's X operands
+    auto mma_kblock = [&](const u32x4& wfr, const u32x4 (&xfr)[MT]) __attribute__((always_inline)) {
+        // the wave's own LDS operations complete in order: the reads see
+        // these writes, and the next k-block's writes land after them
+        u32x4 xo[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (XT)
+                xslot[wave][mt][xw] = xfr[mt];
+            else
+                xo[mt] = xfr[mt];
+        }
+        if constexpr (XT) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xo[mt] = xslot[wave][mt][xr];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[mt], wfr, xo[mt]);
+    };
+
+    // Whole batches inside K: the weight rows load as whole rows (load j of
+    // a span: row n0 + 4 j + lane / 16, 16-byte unit lane % 16; rows past N
+    // clamped, never stored) and each span's 16 rows go through the wave's
+    // slot into operand layout (unit u of row r at r * 16 + (u ^ r):
+    // conflict-free both ways).  In operand layout every load puts 16 rows
+    // under one instruction and 4 under every lane quad, which the memory
+    // pipeline moves at about half the rate.
+    constexpr int NSP = DECODE_BATCH / DSPAN;  // spans per batch
+    const int lr = lane >> 4, lu = lane & 15, orow = lane & 15, ochunk = lane >> 4;
+    const char* wtile = (const char*)p.W + (int64_t)n0 * p.ldw * 2;
+    uint32_t woff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        woff[j] = (uint32_t)((min(n0 + 4 * j + lr, p.N - 1) - n0) * p.ldw * 2 + 16 * lu);
+    int kb = kb0;
+    for (; kb + DECODE_BATCH <= kb1 && (kb + DECODE_BATCH) * 32 <= p.K; kb += DECODE_BATCH) {
+        u32x4 raw[NSP][4], xf[DECODE_BATCH][MT];
+#pragma unroll
+        for (int sp = 0; sp < NSP; ++sp)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                raw[sp][j] = load16(wtile + (int64_t)(kb + DSPAN * sp) * 64 + woff[j]);
+#pragma unroll
+        for (int i = 0; i < DECODE_BATCH; ++i)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xf[i][mt] = load16(xrow[mt] + (int64_t)(kb + i) * 64);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sp = 0; sp < NSP; ++sp) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * j + lr;
+                wslot[wave][r * 16 + (lu ^ r)] = raw[sp][j];
+            }
+            u32x4 wf[DSPAN];
+#pragma unroll
+            for (int i = 0; i < DSPAN; ++i) wf[i] = wslot[wave][orow * 16 + ((4 * i + ochunk) ^ orow)];
+#pragma unroll
+            for (int i = 0; i < DSPAN; ++i) mma_kblock(wf[i], xf[DSPAN * sp + i]);
+        }
+    }
+    // the rest (a short or ragged end of the wave's k-blocks): fragments in
+    // operand layout, masked by k
+    for (; kb < kb1; kb += DECODE_BATCH) {
         u32x4 wf[DECODE_BATCH], xf[DECODE_BATCH][MT];
 #pragma unroll
         for (int i = 0; i < DECODE_BATCH; ++i) {
@@ -104,24 +172,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
                 xf[i][mt] = inx ? load16(xrow[mt] + (int64_t)(kb + i) * 64) : (u32x4){0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < DECODE_BATCH; ++i) {
-            // the wave's own LDS operations complete in order: the reads see
-            // these writes, and the next k-block's writes land after them
-            u32x4 xo[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if constexpr (XT)
-                    xslot[wave][mt][xw] = xf[i][mt];
-                else
-                    xo[mt] = xf[i][mt];
-            }
-            if constexpr (XT) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xo[mt] = xslot[wave][mt][xr];
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[mt], wf[i], xo[mt]);
-        }
+        for (int i = 0; i < DECODE_BATCH; ++i) mma_kblock(wf[i], xf[i]);
     }
 
     // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each block
@@ -178,7 +229,6 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_kernel(DecodeAr
 //    device-scope stores, counter and loads it needs cost ~4 round trips of
 //    ~1.5 us to the memory side, against ~2.7 us for the fixup launch.)
 constexpr int DSPLIT_ROWS = 64;
-constexpr int DSPAN = 4;  // k-blocks per load span
 
 template <int DT, int MT>
 __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(DecodeArgs p) {
