@@ -23,7 +23,10 @@ def _ints(shape, dtype, seed):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(1, 512, 256), (5, 100, 40), (16, 64, 8), (17, 300, 1000),
-                                   (33, 16, 4096), (64, 1040, 520)])
+                                   (33, 16, 4096), (64, 1040, 520),
+                                   # whole-row weight batches: ragged N (clamped rows), two
+                                   # batches per wave, a batch plus a ragged end
+                                   (8, 100, 4096), (16, 256, 8192), (2, 48, 4160), (1, 80, 4096)])
 def test_decode_integer_exact_and_deterministic(M, N, K, dtype):
     X, W = _ints((M, K), dtype, 6000 + M), _ints((N, K), dtype, 6100 + N)
     T, _ = oracle.gemm(X, W, dtype, trans_b=True, want_U=False)
