@@ -6,12 +6,14 @@
 //
 //  * A workgroup owns 16 weight rows and all M input rows; its 8 waves split
 //    K into 8 slices of whole 32-deep k-blocks.  Within a wave, the MFMA "A"
-//    operand is 8 consecutive k of one weight row per lane, i.e. a 16-byte
-//    load straight from W into registers (no LDS), and the "B" operand is 8
-//    consecutive k of one row of X (L2-resident: X is at most 64 x K; for
-//    M > 1 loaded with whole 64-byte row pieces per lane quad and moved
-//    into the operand layout through a small per-wave LDS slot).  The
-//    product is C^T = W X^T in 16 x 16 blocks, MT = ceil(M / 16) of them.
+//    operand is 8 consecutive k of one weight row per lane and the "B"
+//    operand 8 consecutive k of one row of X (L2-resident: X is at most 64 x
+//    K).  Both are loaded in a coalesced layout and moved into the operand
+//    layout through small per-wave LDS slots: the weight as whole rows (4
+//    rows x 256 bytes per load, for whole batches inside K; the ragged end
+//    of a slice loads in operand layout), X for M > 1 as 64-byte row pieces
+//    per lane quad.  The product is C^T = W X^T in 16 x 16 blocks, MT =
+//    ceil(M / 16) of them.
 //  * Loads for 16 k-blocks (8 for M > 32) are issued before their MFMAs, so
 //    each lane keeps up to 256 bytes of W (and of X) in flight; with 8 waves
 //    per CU that is ~128 KB of W per CU, and a 4096-deep K costs each wave a
