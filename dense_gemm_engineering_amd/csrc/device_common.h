@@ -98,6 +98,15 @@ struct Epilogue {
 
 // The fused epilogue on one accumulator value: alpha*acc + beta*old, + bias,
 // then GELU.  `old` is only meaningful when beta != 0.
+// epilogue_value takes the bias value already loaded (read only when epi
+// adds one); both give the same bits for the same inputs.
+__device__ inline float epilogue_value(const Epilogue& e, float acc, float old, float bias) {
+    float t = e.alpha * acc;
+    if (e.beta != 0.0f) t += e.beta * old;
+    if (e.epi != EPI_NONE) t += bias;
+    if (e.epi == EPI_BIAS_GELU) t = gelu_tanh(t);
+    return t;
+}
 template <int DT>
 __device__ inline float apply_epilogue(const Epilogue& e, float acc, float old, int col) {
     float t = e.alpha * acc;

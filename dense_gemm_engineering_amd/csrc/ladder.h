@@ -136,25 +136,54 @@ __global__ __launch_bounds__(256) void splitk_fixup_kernel(SimpleArgs p, const f
 // The same fixup, four consecutive columns per thread: 16-byte partial
 // loads, one 8- or 16-byte store (N % 4 == 0, the workspace 16-byte aligned,
 // C rows and the 4-column groups aligned to their store size).  Each group
-// is summed in the same slice order as above.
+// is summed in the same slice order as above.  A thread requests up to
+// FIXUP_BATCH slices' partials (and its bias and old C values) before it
+// adds any of them: loaded one at a time, each slice cost a whole memory
+// round trip.
+constexpr int FIXUP_BATCH = 8;
+
 template <int DT, int OT>
 __global__ __launch_bounds__(256) void splitk_fixup4_kernel(SimpleArgs p, const float* ws,
                                                             int splits) {
     typedef typename OutType<OT>::T T;
     const int64_t total = (int64_t)p.M * p.N, groups = total / 4;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const bool small = total <= 0xFFFFFFFFll;  // 32-bit row / column arithmetic
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
         const int64_t idx = 4 * g;
-        f32x4 s = *(const f32x4*)(ws + idx);
-        for (int sp = 1; sp < splits; ++sp) s += *(const f32x4*)(ws + sp * total + idx);
-        const int row = (int)(idx / p.N), col = (int)(idx % p.N);
+        const float* w = ws + idx;
+        f32x4 s = *(const f32x4*)w;
+        for (int sp0 = 1; sp0 < splits; sp0 += FIXUP_BATCH) {
+            f32x4 v[FIXUP_BATCH];
+#pragma unroll
+            for (int j = 0; j < FIXUP_BATCH; ++j)
+                if (sp0 + j < splits) v[j] = *(const f32x4*)(w + (int64_t)(sp0 + j) * total);
+#pragma unroll
+            for (int j = 0; j < FIXUP_BATCH; ++j)
+                if (sp0 + j < splits) s += v[j];
+        }
+        int row, col;
+        if (small) {
+            row = (int)((uint32_t)idx / (uint32_t)p.N);
+            col = (int)((uint32_t)idx - (uint32_t)row * (uint32_t)p.N);
+        } else {
+            row = (int)(idx / p.N);
+            col = (int)(idx - (int64_t)row * p.N);
+        }
         T* c = (T*)p.C + (int64_t)row * p.ldc + col;
+        float old[4] = {0.f, 0.f, 0.f, 0.f}, bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.ep.beta != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) old[e] = OutType<OT>::to_f32(c[e]);
+        }
+        if (p.ep.epi != EPI_NONE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bias[e] = load_elem<DT>(p.ep.bias, col + e);
+        }
         T o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float old = p.ep.beta != 0.0f ? OutType<OT>::to_f32(c[e]) : 0.0f;
-            o[e] = OutType<OT>::from_f32(apply_epilogue<DT>(p.ep, s[e], old, col + e));
-        }
+        for (int e = 0; e < 4; ++e)
+            o[e] = OutType<OT>::from_f32(epilogue_value(p.ep, s[e], old[e], bias[e]));
         if constexpr (OutType<OT>::BYTES == 4)
             *(f32x4*)c = (f32x4){o[0], o[1], o[2], o[3]};
         else
