@@ -22,7 +22,7 @@ OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["api.cpp", "kernels_mfma_f16.hip", "kernels_mfma_bf16.hip", "kernels_mfma_f32.hip",
            "kernels_direct_f16.hip", "kernels_direct_bf16.hip",
-           "kernels_misc.hip", "kernels_skinny.hip", "kernels_q4.hip",
+           "kernels_misc.hip", "kernels_skinny.hip", "kernels_skinny_fold.hip", "kernels_q4.hip",
            "kernels_decode.hip", "kernels_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -59,9 +59,14 @@ hipError_t launch_mfma_q4_f16(int tile, const MfmaArgs& a, int nwg, hipStream_t 
 // workgroup (1..16), lds = dynamic LDS bytes (skinny_lds_bytes).
 hipError_t launch_skinny(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid, int waves,
                          size_t lds, hipStream_t s);
+// The instances for alpha = 1, beta = 0 and fp16 output, which
+// launch_skinny picks for such arguments (kernels_skinny_fold.hip).
+hipError_t launch_skinny_fold(int dt, int nt, int trans_b, const SkinnyArgs& a, int grid,
+                              int waves, size_t lds, hipStream_t s);
 // Allows every skinny instance up to 160 KB of dynamic LDS.  Called once per
 // device at library initialisation, never from inside a launch sequence.
 hipError_t skinny_init();
+hipError_t skinny_fold_init();
 // Decode-shaped kernel: 1 <= M <= 64, N x K 16-bit weight, one workgroup per
 // 16 weight rows.
 hipError_t launch_decode(int dt, const DecodeArgs& a, hipStream_t s);

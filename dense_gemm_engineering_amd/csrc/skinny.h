@@ -28,6 +28,19 @@
 //    epilogue (alpha/beta, per-column bias, tanh-GELU, rounding) works on 4
 //    adjacent outputs; the rounded tile goes through the wave's LDS staging
 //    area and leaves as whole rows, 16 bytes per lane.
+//  * The vector ALU, not HBM, turned out to bound it: at N = K = 160 a wave
+//    issued ~1870 VALU instructions (the GELU's exp and reciprocal per
+//    output, but also per-chunk index arithmetic for W, zeroing and bias
+//    adds, conversions, 64-bit store addresses, and hoisted masks of the
+//    unused epilogue kinds spilling scalar registers), ~65% of each SIMD's
+//    time, and the cache-warm time was within 3% of the HBM-cold one.  So
+//    W is staged in uniform-stride passes with 32-bit offsets; with alpha =
+//    1, beta = 0 and fp16 output the bias starts the accumulators (separate
+//    instances carrying only that epilogue); pairs are converted with one
+//    packed instruction; and a wave whose rows are one contiguous block of
+//    C stores it at a uniform base plus a 32-bit offset.  N = 160: 14.1 ->
+//    12.4 us (graph replays, HBM-cold X and C, same box, alternating
+//    processes).
 #pragma once
 
 #include "device_common.h"
@@ -77,14 +90,15 @@ __host__ __device__ inline int skinny_pitch(int trans_b, int K) {
 __host__ __device__ inline size_t skinny_w_bytes(int trans_b, int nt, int K) {
     return trans_b ? (size_t)nt * 16 * (K + 8) * 2 : (size_t)skinny_cblocks(nt) * K * SKINNY_CB * 2;
 }
-// Dynamic LDS: W, the bias (NT*16 fp32), then one output staging tile per
-// wave (RB*16 rows x (NT*16*out_bytes + 16) bytes).
+// Dynamic LDS: W, the bias (NT*16 fp32), the accumulators' starting row
+// (NT*16 fp32), then one output staging tile per wave (RB*16 rows x
+// (NT*16*out_bytes + 16) bytes).
 __host__ __device__ inline size_t skinny_stage_bytes(int nt, int out_bytes) {
     return (size_t)16 * skinny_rb(nt) * (nt * 16 * out_bytes + 16);
 }
 __host__ __device__ inline size_t skinny_lds_bytes(int trans_b, int nt, int K, int out_bytes,
                                                    int waves) {
-    return skinny_w_bytes(trans_b, nt, K) + (size_t)nt * 16 * 4 +
+    return skinny_w_bytes(trans_b, nt, K) + (size_t)nt * 16 * 8 +
            (size_t)waves * skinny_stage_bytes(nt, out_bytes);
 }
 // Waves per workgroup: the most (8, 4, 2 or 1) whose staging fits 160 KB.
@@ -124,10 +138,13 @@ __device__ inline void skinny_load4(const SkinnyArgs& p, int m, int n0, float* t
 // rows of C.
 // The epilogue kind is a template argument (EPI): with it a runtime flag,
 // the compiler evaluated bias and GELU for every output and selected.
-template <int OT, int NT, int RB, int EPI>
+// GEN = false is the case alpha = 1, beta = 0: the accumulators started from
+// the bias (or zero), so the value before GELU is the accumulator itself.
+template <int OT, int NT, int RB, int EPI, bool GEN>
 __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB][NT],
                                      const float* bias_s, int base, int lane, char* stage) {
     typedef typename OutType<OT>::T T;
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
     constexpr int OB = OutType<OT>::BYTES;
     constexpr int pitch_o = NT * 16 * OB + 16;
 #pragma unroll
@@ -137,24 +154,34 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB]
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n0 = nt * 16 + 4 * (lane >> 4);
-            f32x4 b = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (EPI != EPI_NONE) b = *(const f32x4*)(bias_s + n0);  // zero past N
             float t[4];
-            if (p.ep.beta != 0.0f) {  // wave-uniform; a branch around loads of C
-                float old[4] = {0.f, 0.f, 0.f, 0.f};
-                if (m < p.M && n0 < p.N) skinny_load4<OT>(p, m, n0, old);
+            if constexpr (GEN) {
+                f32x4 b = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (EPI != EPI_NONE) b = *(const f32x4*)(bias_s + n0);  // zero past N
+                if (p.ep.beta != 0.0f) {  // wave-uniform; a branch around loads of C
+                    float old[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (m < p.M && n0 < p.N) skinny_load4<OT>(p, m, n0, old);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = p.ep.alpha * acc[rb][nt][e] + p.ep.beta * old[e] + b[e];
+                    for (int e = 0; e < 4; ++e) t[e] = p.ep.alpha * acc[rb][nt][e] + p.ep.beta * old[e] + b[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf(p.ep.alpha, acc[rb][nt][e], b[e]);
+                }
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf(p.ep.alpha, acc[rb][nt][e], b[e]);
+                for (int e = 0; e < 4; ++e) t[e] = acc[rb][nt][e];
             }
             if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) t[e] = gelu_tanh(t[e]);
             }
             char* dst = stage + ml * pitch_o + n0 * OB;
-            if constexpr (OB == 2) {
+            if constexpr (OT == OUT_F16) {
+                // one packed conversion per pair (round to nearest even)
+                const h2_t lo = {(_Float16)t[0], (_Float16)t[1]};
+                const h2_t hi = {(_Float16)t[2], (_Float16)t[3]};
+                *(uint2*)dst = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+            } else if constexpr (OB == 2) {
                 const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[0])) |
                                     ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[1])) << 16);
                 const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[2])) |
@@ -174,23 +201,44 @@ __device__ inline void skinny_finish(const SkinnyArgs& p, const f32x4 (&acc)[RB]
     // q % cpr); stepped without a division per chunk
     const int d_row = 64 / cpr, d_chunk = 64 - d_row * cpr;
     int r = lane / cpr, c = lane - r * cpr;
-    while (r < RB * 16) {
-        const int mm = base + r;
-        if (mm < p.M) {
-            const char* src = stage + r * pitch_o + c * 16;
-            char* dst = (char*)p.C + ((int64_t)mm * p.ldc) * OB + c * 16;
-            if (vec) {
-                __builtin_nontemporal_store(*(const u32x4*)src, (u32x4*)dst);
-            } else {
-                for (int e = 0; e < 16 / OB; ++e)
-                    if (c * 16 + e * OB < row_bytes) ((T*)dst)[e] = ((const T*)src)[e];
+    if (vec && p.ldc == p.N && base + RB * 16 <= p.M) {
+        // the wave's rows are one contiguous block of C: chunk q sits q * 16
+        // bytes past the block's start (a uniform address, a 32-bit offset)
+        constexpr int QMAX = (RB * 16 * NT * 16 * OB / 16 + 63) / 64;  // chunks per lane at most
+        const int total = RB * 16 * cpr;
+        char* blk = (char*)p.C + (int64_t)base * p.ldc * OB;
+#pragma unroll
+        for (int i = 0; i < QMAX; ++i) {
+            const int q = lane + 64 * i;
+            if (q < total)
+                __builtin_nontemporal_store(*(const u32x4*)(stage + r * pitch_o + c * 16),
+                                            (u32x4*)(blk + (uint32_t)q * 16u));
+            r += d_row;
+            c += d_chunk;
+            if (c >= cpr) {
+                c -= cpr;
+                ++r;
             }
         }
-        r += d_row;
-        c += d_chunk;
-        if (c >= cpr) {
-            c -= cpr;
-            ++r;
+    } else {
+        while (r < RB * 16) {
+            const int mm = base + r;
+            if (mm < p.M) {
+                const char* src = stage + r * pitch_o + c * 16;
+                char* dst = (char*)p.C + ((int64_t)mm * p.ldc) * OB + c * 16;
+                if (vec) {
+                    __builtin_nontemporal_store(*(const u32x4*)src, (u32x4*)dst);
+                } else {
+                    for (int e = 0; e < 16 / OB; ++e)
+                        if (c * 16 + e * OB < row_bytes) ((T*)dst)[e] = ((const T*)src)[e];
+                }
+            }
+            r += d_row;
+            c += d_chunk;
+            if (c >= cpr) {
+                c -= cpr;
+                ++r;
+            }
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -200,11 +248,11 @@ template <int NT, int RB, int EPI>
 __device__ inline void skinny_finish_ot(const SkinnyArgs& p, const f32x4 (&acc)[RB][NT],
                                         const float* bias_s, int base, int lane, char* stage) {
     if (p.c_type == OUT_F16)
-        skinny_finish<OUT_F16, NT, RB, EPI>(p, acc, bias_s, base, lane, stage);
+        skinny_finish<OUT_F16, NT, RB, EPI, true>(p, acc, bias_s, base, lane, stage);
     else if (p.c_type == OUT_BF16)
-        skinny_finish<OUT_BF16, NT, RB, EPI>(p, acc, bias_s, base, lane, stage);
+        skinny_finish<OUT_BF16, NT, RB, EPI, true>(p, acc, bias_s, base, lane, stage);
     else
-        skinny_finish<OUT_F32, NT, RB, EPI>(p, acc, bias_s, base, lane, stage);
+        skinny_finish<OUT_F32, NT, RB, EPI, true>(p, acc, bias_s, base, lane, stage);
 }
 
 // W into LDS by nth threads, one batch (BT tasks per thread) at a time:
@@ -271,6 +319,52 @@ struct WStage {
     }
 };
 
+// A K x N W with N a multiple of 8, 16-byte aligned rows and byte offsets
+// below 2^32: thread tid owns chunk column c = tid % PR (PR = NT * 2 chunks
+// of the NT*16 staged columns, zeros past N) of k-rows r0 + RP i (r0 = tid /
+// PR, RP = nth / PR rows a pass; threads past RP * PR stage nothing).  The
+// passes, and the threads' rows within a pass, run in a per-workgroup
+// rotated order (every workgroup wants all of W at the same moment;
+// starting at different rows spreads the requests over the cache channels),
+// so a pass's row and offsets are a uniform shift of the thread's first: a
+// few VALU instructions per 16-byte chunk, against several dozen with a
+// division and 64-bit addresses per chunk.
+template <int NT>
+__device__ inline void skinny_stage_w_kn(const SkinnyArgs& p, uint16_t* wt, int tid, int nth) {
+    constexpr int PR = NT * 2, BT = 8;
+    const int RP = nth / PR, K = p.K;
+    const int c = tid % PR;
+    int r0 = tid / PR;
+    if (r0 >= RP) return;
+    r0 += (int)((blockIdx.x * 13u) % (unsigned)RP);  // first rows rotated too
+    if (r0 >= RP) r0 -= RP;
+    const bool live = c * 8 < p.N;
+    const int NI = (K + RP - 1) / RP;  // passes
+    const int irot = (int)(blockIdx.x % (unsigned)NI);
+    const uint32_t ldw2 = (uint32_t)p.ldw * 2u;
+    const uint32_t goff0 = (uint32_t)r0 * ldw2 + (uint32_t)c * 16u;
+    char* lblk = (char*)wt + (c >> 3) * K * SKINNY_CB * 2;
+    for (int i0 = 0; i0 < NI; i0 += BT) {
+        u32x4 v[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            v[j] = (u32x4){0, 0, 0, 0};
+            int ip = i0 + j + irot;
+            if (ip >= NI) ip -= NI;
+            if (i0 + j < NI && live && r0 + ip * RP < K)
+                v[j] = load16((const char*)p.W + (goff0 + (uint32_t)(ip * RP) * ldw2));
+        }
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            int ip = i0 + j + irot;
+            if (ip >= NI) ip -= NI;
+            const int row = r0 + ip * RP;
+            if (i0 + j < NI && row < K)
+                *(u32x4*)(lblk + row * (SKINNY_CB * 2) + 16 * ((c & 7) ^ swz_kn(row))) = v[j];
+        }
+    }
+}
+
 // The X operand registers of k-blocks kb0 .. kb0 + KCH - 1 of one wave's
 // RB x 16 rows starting at row base.  (Loading whole rows and moving them
 // into operand layout through LDS, as the decode kernel does for its
@@ -290,7 +384,9 @@ __device__ inline void skinny_load_x(const SkinnyArgs& p, int base, int kb0, int
     }
 }
 
-template <int DT, int NT, bool TRANS_B>
+// FOLD: alpha = 1, beta = 0 and fp16 output (the launcher's choice), the
+// bias starting the accumulators; the other instances take any epilogue.
+template <int DT, int NT, bool TRANS_B, bool FOLD>
 __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(SkinnyArgs p) {
     extern __shared__ __attribute__((aligned(16))) uint16_t wt[];  // NT*16 rows x pitch
     constexpr int RB = skinny_rb(NT);
@@ -311,26 +407,40 @@ __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(
     // wave requests its rows of X and starts its MFMAs as soon as they
     // arrive, so later rows' loads overlap earlier rows' stores.
     const int nth = blockDim.x;
-    WStage<DT, NT, TRANS_B> wst;
-    const int w_tasks = WStage<DT, NT, TRANS_B>::ntask(p);
-    const int rot = (int)(((int64_t)blockIdx.x * 97 * 64) % w_tasks);
-    wst.load(p, 0, tid, nth, rot);
     uint32_t bias_bits[4];  // NT * 16 <= 256 values over at least 64 threads
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = tid + i * nth;
         bias_bits[i] = p.ep.epi != EPI_NONE && n < p.N ? load_elem_bits<DT>(p.ep.bias, n) : 0u;
     }
-    wst.store(p, wt, 0, tid, nth, rot);
-    const int w_batch = WStage<DT, NT, TRANS_B>::BT * nth;
-    for (int t0 = w_batch; t0 < w_tasks; t0 += w_batch) {
-        wst.load(p, t0, tid, nth, rot);
-        wst.store(p, wt, t0, tid, nth, rot);
+    bool fast_w = false;
+    if constexpr (!TRANS_B)
+        fast_w = (p.vec_c & 2) != 0 && p.N % 8 == 0 && p.K * p.ldw * 2 < (int64_t)1 << 32;
+    if (fast_w) {
+        skinny_stage_w_kn<NT>(p, wt, tid, nth);
+    } else {
+        WStage<DT, NT, TRANS_B> wst;
+        const int w_tasks = WStage<DT, NT, TRANS_B>::ntask(p);
+        const int rot = (int)(((int64_t)blockIdx.x * 97 * 64) % w_tasks);
+        const int w_batch = WStage<DT, NT, TRANS_B>::BT * nth;
+        for (int t0 = 0; t0 < w_tasks; t0 += w_batch) {
+            wst.load(p, t0, tid, nth, rot);
+            wst.store(p, wt, t0, tid, nth, rot);
+        }
     }
+    // FOLD: the accumulators start from the bias (init_s), and the epilogue
+    // adds nothing; otherwise they start from zero and the epilogue applies
+    // alpha, beta and the bias (bias_s)
+    constexpr bool fold = FOLD;
     float* bias_s = (float*)((char*)wt + skinny_w_bytes(TRANS_B, NT, p.K));
+    float* init_s = bias_s + NT * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        if (tid + i * nth < NT * 16) bias_s[tid + i * nth] = InType<DT>::to_f32(bias_bits[i]);
+        if (tid + i * nth < NT * 16) {
+            const float b = InType<DT>::to_f32(bias_bits[i]);
+            bias_s[tid + i * nth] = b;
+            init_s[tid + i * nth] = fold ? b : 0.0f;
+        }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
     __builtin_amdgcn_s_barrier();
     if (rec) t_w = __builtin_amdgcn_s_memrealtime();
@@ -361,13 +471,14 @@ __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(
         }
     }
     const int ob = p.c_type == OUT_F32 ? 4 : 2;
-    char* stage = (char*)(bias_s + NT * 16) + wave * skinny_stage_bytes(NT, ob);
+    char* stage = (char*)(init_s + NT * 16) + wave * skinny_stage_bytes(NT, ob);
     for (; base < p.M; base += rows_per_step) {
         f32x4 acc[RB][NT];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[rb][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NT; ++nt)
+                acc[rb][nt] = *(const f32x4*)(init_s + nt * 16 + 4 * (lane >> 4));
 #pragma unroll
         for (int c0 = 0; c0 < SKINNY_KBMAX; c0 += KCH) {
             if (c0 >= KB) break;
@@ -406,12 +517,19 @@ __global__ __launch_bounds__(skinny_max_waves(NT) * 64) void gemm_skinny_kernel(
         }
         // the next rows' loads overlap this epilogue's stores
         if (base + rows_per_step < p.M) skinny_load_x<RB, KCH>(p, base + rows_per_step, 0, lane, xf);
-        if (p.ep.epi == EPI_BIAS_GELU)
+        if constexpr (FOLD) {
+            // alpha = 1, beta = 0, fp16 out: the bias is already in acc
+            if (p.ep.epi == EPI_BIAS_GELU)
+                skinny_finish<OUT_F16, NT, RB, EPI_BIAS_GELU, false>(p, acc, bias_s, base, lane, stage);
+            else
+                skinny_finish<OUT_F16, NT, RB, EPI_NONE, false>(p, acc, bias_s, base, lane, stage);
+        } else if (p.ep.epi == EPI_BIAS_GELU) {
             skinny_finish_ot<NT, RB, EPI_BIAS_GELU>(p, acc, bias_s, base, lane, stage);
-        else if (p.ep.epi == EPI_BIAS)
+        } else if (p.ep.epi == EPI_BIAS) {
             skinny_finish_ot<NT, RB, EPI_BIAS>(p, acc, bias_s, base, lane, stage);
-        else
+        } else {
             skinny_finish_ot<NT, RB, EPI_NONE>(p, acc, bias_s, base, lane, stage);
+        }
     }
     if (rec) {
         // start, W staged (barrier passed), wave 0's first rows landed, wave 0's

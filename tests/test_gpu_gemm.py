@@ -368,6 +368,38 @@ def test_skinny_kernel(M, N, K, trans_b, dtype):
         assert_close(C, T, U, 1.25, what=epi)
 
 
+# alpha = 1, beta = 0 with fp16 output takes the instances whose accumulators
+# start from the bias (no epilogue add); other outputs keep the general ones.
+# Integer bias: exact either way.  A C with a row pitch wider than N takes
+# the row-by-row stores instead of the contiguous-block ones.
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("M,N,K", [(5000, 160, 160), (4096, 32, 160), (1000, 70, 96)])
+def test_skinny_bias_in_accumulators(M, N, K, trans_b):
+    Ai, Bi = _operands(M, N, K, "f16", trans_b, True, 1700 + N)
+    r = np.random.Generator(np.random.PCG64(1701 + N))
+    bias_i = r.integers(-8, 9, N).astype(np.float64)
+    Ti, _ = oracle.gemm(Ai, Bi, "f16", trans_b=trans_b, epi="bias", bias=bias_i)
+    C = dge.gemm_ex(to_dev(Ai, "f16"), to_dev(Bi, "f16"), trans_b=trans_b, epi="bias",
+                    bias=to_dev(inputs.to_bits(bias_i, "f16"), "f16"), algo="skinny")
+    torch.cuda.synchronize()
+    assert_bits(C, Ti, what="integer bias")
+    wide = torch.full((M, N + 24), 7.0, dtype=torch.float16, device="cuda")
+    dge.gemm_ex(to_dev(Ai, "f16"), to_dev(Bi, "f16"), wide[:, :N], trans_b=trans_b, epi="bias",
+                bias=to_dev(inputs.to_bits(bias_i, "f16"), "f16"), algo="skinny")
+    torch.cuda.synchronize()
+    assert_bits(wide[:, :N], Ti, what="integer bias, ldc > N")
+    assert bool((wide[:, N:] == 7.0).all()), "columns past N written"
+    A, B = _operands(M, N, K, "f16", trans_b, False, 1750 + N)
+    bias_bits = inputs.to_bits(r.normal(0, 0.1, N), "f16")
+    bias = oracle.decode(bias_bits, "f16")
+    T, U = oracle.gemm(A, B, "f16", trans_b=trans_b, epi="bias_gelu", bias=bias)
+    for out in (torch.float16, torch.bfloat16):
+        C = dge.gemm_ex(to_dev(A, "f16"), to_dev(B, "f16"), trans_b=trans_b, out_dtype=out,
+                        epi="bias_gelu", bias=to_dev(bias_bits, "f16"), algo="skinny")
+        torch.cuda.synchronize()
+        assert_close(C, T, U, 1.0, what="bias_gelu %s" % out)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("out", [torch.float16, torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("trans_b", [False, True])
