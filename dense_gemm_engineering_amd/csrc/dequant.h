@@ -129,8 +129,10 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
                                                              int64_t ldo, int flags) {
     constexpr int BYTES = KQuant<QT>::BYTES;
     static_assert(SB % 8 == 0, "groups of 8 super-blocks keep 16-byte alignment");
-    __shared__ __attribute__((aligned(16))) uint8_t raw[SB * BYTES];
+    // (16 spare bytes: the q4_0 decode reads whole dwords past a block's end)
+    __shared__ __attribute__((aligned(16))) uint8_t raw[SB * BYTES + 16];
     const bool vec_in = (flags & 1) != 0, vec_out = (flags & 2) != 0;
+    const bool off32 = (flags & 4) != 0;  // (SB + 1) rows of out span < 2^31 bytes
     const int tid = threadIdx.x;
     const int64_t nsb = cols / 256;
     const int64_t total = rows * nsb;
@@ -166,6 +168,9 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
         // first super-block of the step: row r0, column c0 (one 64-bit division per step)
         const int64_t r0 = g0 / nsb;
         const uint32_t c0 = (uint32_t)(g0 - r0 * nsb), unsb = (uint32_t)nsb;
+        uint16_t* orow = out + r0 * ldo;  // row r0 of the output
+        const bool wide = nsb >= SB;      // a step then crosses at most one row end
+        const uint32_t ldo32 = (uint32_t)ldo;
         __syncthreads();
         if (vec_in && g0 + gstep < total) fetch(g0 + gstep);
         for (int task = tid; task < 32 * nblk; task += 256) {
@@ -173,20 +178,42 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
             const uint8_t* blk = raw + BYTES * sbl;
             const int e0 = 8 * c;
             uint16_t h[8];
+            uint32_t hw[4];  // the eight results as pairs (the q4_0 path)
             if constexpr (QT == KQ_Q4_0_256) {
                 // chunk c % 4 of q4_0 block c / 4 of the group: the low (chunk
-                // < 2) or high nibbles of code bytes 8 (chunk & 1) .. + 7
-                const uint8_t* b = blk + 18 * (c >> 2);
+                // < 2) or high nibbles of code bytes 8 (chunk & 1) .. + 7.
+                // The block starts at an even byte o; its fields are read as
+                // whole dwords from o rounded down to 4 and aligned with
+                // alignbit.  Each code becomes the binary16 1024 + q by
+                // placing the byte 0x64 above it, minus 1032 is q - 8 exactly,
+                // and one packed multiply by d rounds d (q - 8) once: the same
+                // bits as the binary32 product rounded to binary16.
                 const int p = c & 3;
-                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[0] | (b[1] << 8)));
-                const uint8_t* qs = b + 2 + 8 * (p & 1);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int code = p < 2 ? (qs[i] & 15) : (qs[i] >> 4);
-                    float v = d * (float)(code - 8);  // exact; one rounding below
-                    __asm__("" : "+v"(v));  // a multiply, not a mixed-precision FMA
-                    h[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                const int o = BYTES * sbl + 18 * (c >> 2);
+                const uint32_t* rw = (const uint32_t*)(raw + (o & ~3));
+                const uint32_t hs = (uint32_t)(o & 2) * 8;  // 0 or 16 bits
+                const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(rw[0] >> hs));
+                const int rel = (o & 2) + 2 + 8 * (p & 1);  // code bytes past o & ~3
+                const uint32_t w0 = rw[rel >> 2], w1 = rw[(rel >> 2) + 1], w2 = rw[(rel >> 2) + 2];
+                const uint32_t bs = (uint32_t)(rel & 3) * 8;
+                uint32_t c03 = __builtin_amdgcn_alignbit(w1, w0, bs);  // code bytes 0-3
+                uint32_t c47 = __builtin_amdgcn_alignbit(w2, w1, bs);  // code bytes 4-7
+                if (p >= 2) {
+                    c03 >>= 4;
+                    c47 >>= 4;
                 }
+                c03 &= 0x0F0F0F0Fu;
+                c47 &= 0x0F0F0F0Fu;
+                typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+                const h2_t off = {(_Float16)1032.0f, (_Float16)1032.0f}, d2 = {d, d};
+                // perm selectors: 0-3 pick bytes of the codes, 4 the byte 0x64
+                const uint32_t v[4] = {__builtin_amdgcn_perm(0x64646464u, c03, 0x04010400u),
+                                       __builtin_amdgcn_perm(0x64646464u, c03, 0x04030402u),
+                                       __builtin_amdgcn_perm(0x64646464u, c47, 0x04010400u),
+                                       __builtin_amdgcn_perm(0x64646464u, c47, 0x04030402u)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    hw[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2_t, v[i]) - off) * d2);
             } else if constexpr (KQuant<QT>::Q6) {
                 const int hh = e0 / 128, tt = (e0 % 128) / 32, l0 = e0 % 32;
                 const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[208] | (blk[209] << 8)));
@@ -232,15 +259,28 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
                     h[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
                 }
             }
+            if constexpr (QT != KQ_Q4_0_256) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hw[i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
+            }
             const uint32_t cc = c0 + (uint32_t)sbl;  // < nsb + SB
-            const uint32_t dr = cc / unsb;
-            uint16_t* dst = out + (r0 + dr) * ldo + 256 * (cc - dr * unsb) + e0;
+            uint16_t* dst;
+            if (off32 && wide) {
+                // row r0 or r0 + 1: a 32-bit offset from row r0
+                const uint32_t off = cc >= unsb ? ldo32 + 256u * (cc - unsb) : 256u * cc;
+                dst = orow + (off + (uint32_t)e0);
+            } else {
+                const uint32_t dr = cc / unsb;
+                dst = out + (r0 + dr) * ldo + 256 * (cc - dr * unsb) + e0;
+            }
             if (vec_out) {
-                *(u32x4*)dst = (u32x4){(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
-                                       (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16)};
+                *(u32x4*)dst = (u32x4){hw[0], hw[1], hw[2], hw[3]};
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) dst[i] = h[i];
+                for (int i = 0; i < 4; ++i) {
+                    dst[2 * i] = (uint16_t)(hw[i] & 0xFFFFu);
+                    dst[2 * i + 1] = (uint16_t)(hw[i] >> 16);
+                }
             }
         }
         __syncthreads();

@@ -102,7 +102,8 @@ hipError_t launch_dequant_kq(int qtype, const void* q, void* out, int64_t rows, 
     // 8 resident workgroups per CU of a 256-CU part: each takes several
     // steps, so its register prefetch of the next step overlaps the decode
     if (blocks > KQ_GRID) blocks = KQ_GRID;
-    const int flags = (((uintptr_t)q & 15) == 0 ? 1 : 0) | (vec_out ? 2 : 0);
+    const int flags = (((uintptr_t)q & 15) == 0 ? 1 : 0) | (vec_out ? 2 : 0) |
+                      ((int64_t)(SB + 1) * ldo * 2 < ((int64_t)1 << 31) ? 4 : 0);
     if (qtype == KQ_Q6_K)
         hipLaunchKernelGGL((dequant_kq_f16_kernel<KQ_Q6_K, SB>), dim3((unsigned)blocks), dim3(256), 0,
                            s, (const uint8_t*)q, (uint16_t*)out, rows, cols, ldo, flags);
