@@ -215,19 +215,37 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
                 for (int i = 0; i < 4; ++i)
                     hw[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(h2_t, v[i]) - off) * d2);
             } else if constexpr (KQuant<QT>::Q6) {
+                // eight consecutive weights share tt, hh and the scale: their
+                // low bits are 8 consecutive ql bytes and their high bits 8
+                // consecutive qh bytes, read as dwords (the block starts at an
+                // even byte o) and combined four codes to a dword
                 const int hh = e0 / 128, tt = (e0 % 128) / 32, l0 = e0 % 32;
-                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(blk[208] | (blk[209] << 8)));
+                const int o = BYTES * sbl;
+                const uint32_t* rw = (const uint32_t*)(raw + (o & ~3));
+                const uint32_t bs = (uint32_t)(o & 2) * 8;  // 0 or 16 bits
+                const int rl = (o & 2) + 64 * hh + 32 * (tt & 1) + l0;  // ql bytes past o & ~3
+                const int rh = (o & 2) + 128 + 32 * hh + l0;            // qh bytes
+                const int rd = (o & 2) + 208;                           // d
+                uint32_t lo03 = __builtin_amdgcn_alignbit(rw[(rl >> 2) + 1], rw[rl >> 2], bs);
+                uint32_t lo47 = __builtin_amdgcn_alignbit(rw[(rl >> 2) + 2], rw[(rl >> 2) + 1], bs);
+                const uint32_t hi03 = __builtin_amdgcn_alignbit(rw[(rh >> 2) + 1], rw[rh >> 2], bs);
+                const uint32_t hi47 = __builtin_amdgcn_alignbit(rw[(rh >> 2) + 2], rw[(rh >> 2) + 1], bs);
+                if (tt >= 2) {
+                    lo03 >>= 4;
+                    lo47 >>= 4;
+                }
+                const uint32_t q03 = (lo03 & 0x0F0F0F0Fu) | (((hi03 >> (2 * tt)) & 0x03030303u) << 4);
+                const uint32_t q47 = (lo47 & 0x0F0F0F0Fu) | (((hi47 >> (2 * tt)) & 0x03030303u) << 4);
+                const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(rw[rd >> 2] >> bs));
                 const float dsc = d * (float)(int8_t)blk[192 + 8 * hh + 2 * tt + l0 / 16];  // exact
-                const uint8_t* ql = blk + 64 * hh + 32 * (tt & 1) + l0;
-                const uint8_t* qh = blk + 128 + 32 * hh + l0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int low = tt < 2 ? (ql[i] & 15) : (ql[i] >> 4);
-                    const int code = (low | (((qh[i] >> (2 * tt)) & 3) << 4)) - 32;
+                    const uint32_t qw = i < 4 ? q03 : q47;
+                    const float code = (float)((qw >> (8 * (i & 3))) & 0xFFu) - 32.0f;  // exact
                     // exact product, one rounding; the empty asm keeps the
                     // multiply a multiply (folded into a mixed-precision FMA it
                     // adds +0, which turns a -0 product into +0)
-                    float v = dsc * (float)code;
+                    float v = dsc * code;
                     __asm__("" : "+v"(v));
                     h[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
                 }
@@ -245,10 +263,16 @@ __global__ __launch_bounds__(256) void dequant_kq_f16_kernel(const uint8_t* __re
                     m = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
                 }
                 const float a = d * (float)sc, u = dmin * (float)m;  // both exact
-                const uint8_t* qs = blk + 16 + 32 * p + (w0 & 31);
+                // the 8 code bytes (16-byte-aligned block, 8-aligned bytes): one
+                // 8-byte read, the low or high nibbles of each byte
+                uint2 qw = *(const uint2*)(blk + 16 + 32 * p + (w0 & 31));
+                if (w0 >= 32) {
+                    qw.x >>= 4;
+                    qw.y >>= 4;
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int code = w0 < 32 ? (qs[i] & 15) : (qs[i] >> 4);
+                    const uint32_t code = ((i < 4 ? qw.x : qw.y) >> (8 * (i & 3))) & 15u;
                     // a * code is exact, so the fused form rounds the difference
                     // once, to binary32; the empty asm keeps that binary32 value
                     // (otherwise the compiler folds fma and conversion into one
