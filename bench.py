@@ -543,11 +543,17 @@ def bench_ladder(dge, inputs, torch, steps):
         A, B = inputs.fp32_square(n)
         dA, dB = _dev(A, "f32", torch), _dev(B, "f32", torch)
         C = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        # the MFMA rung gets the workspace the library asks for (a K split
+        # fills the CUs at n = 1024)
+        wsz = dge.gemm_workspace_size(n, n, n, torch.float32)
+        ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device="cuda") if wsz else None
         row = {}
         algos = ["naive", "lds_tiled", "mfma"] if n <= 2048 else ["lds_tiled", "mfma"]
         for algo in algos:
             s = max(2, steps // 10) if algo != "mfma" else steps
-            t = time_leg(lambda: dge.gemm_ex(dA, dB, C, algo=algo), s, torch, warm_seconds=0.1)
+            w = ws if algo == "mfma" else None
+            t = time_leg(lambda: dge.gemm_ex(dA, dB, C, algo=algo, workspace=w), s, torch,
+                         warm_seconds=0.1)
             tf = gemm_flops(n, n, n) / (t["us"] * 1e-6) / 1e12
             row[algo] = {"us": t["us"], "TFLOPs": tf, "fp32_mfma_frac": tf / PEAK["f32"],
                          "timing": t}

@@ -233,6 +233,36 @@ double schedule_us(int64_t M, int64_t N, int64_t K, int tile, int splits, int bk
     return us;
 }
 
+// fp32 inputs: the fp32 MFMA rate bounds every tile (16x16x4 blocks at a
+// sixteenth of the 16-bit rate), so a schedule takes the busiest CU's FLOPs
+// at the tile's per-CU rate, plus a fixed cost per launch and, for a split,
+// the fixup pass.  Per-CU rates fitted on MI355X to M = N = K = 1024, 2048
+// and 4096 over every tile and split (e.g. 4096^3: 8-wave 256 x 256 982 us,
+// 128 x 64 1127 us; 2048^3: 128 x 64 154 us, 8-wave 256 x 256 split 4 156
+// us; 1024^3: 128 x 64 split 2 34 us); the 16-bit model above, whose partly
+// filled rounds run faster for power, picked half-filled grids here (2048^3
+// in 299 us).
+double tile_rate_f32(int tile) {  // TFLOP/s per CU
+    switch (tile) {
+        case TILE_256x256_W8: return 0.554;
+        case TILE_256x256: return 0.41;
+        case TILE_128x128: return 0.47;
+        case TILE_128x64: return 0.48;
+        default: return 0.46;  // 256 x 128 (both ids run the 4-wave kernel)
+    }
+}
+double schedule_us_f32(int64_t M, int64_t N, int64_t K, int tile, int splits, int bk, int cus) {
+    const TileShape ts = tile_shape(tile);
+    const int64_t work = (int64_t)ceil_div(M, ts.bm) * ceil_div(N, ts.bn) * splits;
+    const int64_t per_cu = (work + cus - 1) / cus;
+    const int64_t k_slice = (int64_t)ceil_div(ceil_div(K, bk), splits) * bk;
+    const double flops = 2.0 * ts.bm * ts.bn * (double)k_slice * (double)per_cu;
+    double us = 12.0 + flops / (tile_rate_f32(tile) * 1e6);
+    // the fixup's partial traffic at ~4 TB/s (2048^3 split 4: ~23 us)
+    if (splits > 1) us += (double)(4 * splits + 4) * (double)M * (double)N / 4.0e6;
+    return us;
+}
+
 // Persistent schedule with a stream-K tail (direct-to-LDS kernels): the grid
 // is every CU slot the tile allows (at most one workgroup per iteration).
 // Its time is R whole-tile rounds plus the tail's ceil(I / G) stages, plus
@@ -315,7 +345,8 @@ void choose_schedule(int64_t M, int64_t N, int64_t K, int dt, int cus, size_t ws
             if (*splits > 0 && sp != *splits) continue;
             if (sp > 1 && (K / sp < 16 * (int64_t)bk || ws_bytes < ws_bytes_for(M, N, sp)))
                 continue;
-            const double us = schedule_us(M, N, K, t, sp, bk, cus);
+            const double us = dt == IN_F32 ? schedule_us_f32(M, N, K, t, sp, bk, cus)
+                                           : schedule_us(M, N, K, t, sp, bk, cus);
             if (us < best * 0.999) {
                 best = us;
                 best_t = t;
