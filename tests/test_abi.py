@@ -130,6 +130,17 @@ def test_workspace_sizes():
     assert dge.gemm_workspace_size(0, 5, 5) == 0
 
 
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="pins the 256-CU choices")
+def test_fp32_schedule_choices():
+    # the fp32 model (FLOPs of the busiest CU at each tile's rate): 1024^3
+    # splits K in two (128 x 64 tiles fill only half the CUs), 2048^3 and
+    # 4096^3 fill the CUs without a split
+    f32 = torch.float32
+    assert dge.gemm_workspace_size(1024, 1024, 1024, f32) == 2 * 1024 * 1024 * 4
+    assert dge.gemm_workspace_size(2048, 2048, 2048, f32) == 0
+    assert dge.gemm_workspace_size(4096, 4096, 4096, f32) == 0
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
 def test_no_device_reports_device_error():
     assert dge.lib().gemm_init() == 5
