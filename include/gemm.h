@@ -147,7 +147,8 @@ typedef enum {
                                  full tiles, K % 64 == 0, aligned operands and
                                  gemm_workspace_size_streamk() bytes of 16-byte
                                  aligned workspace (GEMM_ERR_WORKSPACE with less);
-                                 other problems run as GEMM_ALGO_MFMA_DIRECT.  AUTO
+                                 other problems, and the 128 x 64 tile with a K x N
+                                 B, run as GEMM_ALGO_MFMA_DIRECT.  AUTO
                                  does not choose it: on MI355X it measured no faster
                                  than the data-parallel and split-K schedules on
                                  the square and prefill shapes (an XCD's workgroups
