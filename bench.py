@@ -81,7 +81,7 @@ def prefill_stack_tokens_per_s(t_attn, t_up, t_down, tokens=2048, layers=32):
 # leg runs back to back for a while without host syncs (the engine clock
 # needs a few hundred ms of load to settle).  The headline legs run
 # interleaved in a shuffled order, three times over, so that slow drift of
-# the clock or the box affects every leg alike.
+# the clock or the machine affects every leg alike.
 
 MIN_TIMED_S = 0.05  # timed work per leg and repeat (windows are added to reach it)
 
@@ -792,8 +792,8 @@ def main():
                          "--warmup launches, and print their names (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: every GPU box here has one, and the library has "
-              "no multi-GPU path (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
