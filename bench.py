@@ -475,6 +475,31 @@ def bench_streamk(dge, torch, steps):
     return out
 
 
+def bench_library_context(dge, torch, steps):
+    """Context only: torch.matmul (the vendor BLAS, hipBLASLt on ROCm) on the
+    4096^3 fp16 product, K x N and N x K B, beside this library's gemm_f16 on
+    the same operands.  Never used by the library."""
+    n = 4096
+    A = torch.randn(n, n, device="cuda", dtype=torch.float16) / n ** 0.5
+    B = torch.randn(n, n, device="cuda", dtype=torch.float16) / n ** 0.5  # K x N
+    Bt = B.t().contiguous()                                              # N x K
+    C = torch.empty(n, n, device="cuda", dtype=torch.float16)
+    fl = gemm_flops(n, n, n)
+    out = {}
+    for name, lib_fn, own_fn in (
+            ("kxn_b", lambda: torch.matmul(A, B, out=C), lambda: dge.gemm_f16(A, B, C)),
+            ("nxk_b", lambda: torch.matmul(A, Bt.t(), out=C),
+             lambda: dge.gemm_f16(A, Bt, C, trans_b=True))):
+        tl = time_leg(lib_fn, steps, torch)
+        to = time_leg(own_fn, steps, torch)
+        out[name] = {"torch_matmul_us": tl["us"], "gemm_f16_us": to["us"],
+                     "torch_matmul_TFLOPs": fl / tl["us"] / 1e6,
+                     "gemm_f16_TFLOPs": fl / to["us"] / 1e6,
+                     "torch_matmul_timing": tl, "gemm_f16_timing": to}
+    del A, B, Bt, C
+    return out
+
+
 def bench_decode(dge, inputs, torch, steps, peaks, rotate_bytes=300e6):
     """The decode shape: M input rows against one 4096 x 4096 fp16 weight
     (HBM-cold by rotating weight copies); bound by reading W once."""
@@ -895,6 +920,7 @@ def main():
         line["skinny_bias_gelu"] = bench_skinny(dge, inputs, torch, extra_steps, peaks)
         line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps, peaks)
         line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)
+        line["library_context"] = bench_library_context(dge, torch, extra_steps)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(A, B, inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
