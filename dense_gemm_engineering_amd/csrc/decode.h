@@ -235,14 +235,17 @@ constexpr int DSPLIT_ROWS = 64;
 template <int DT, int MT>
 __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(DecodeArgs p) {
     constexpr int NB = DSPLIT_ROWS / 16;  // weight blocks per workgroup
-    // partial C^T blocks [wave][nb][mt][16 n x 16 m]; during the main loop
-    // each wave's part holds its transpose slot.  Each weight block's MT
-    // blocks are padded so that the weight blocks start 16 banks apart: the
-    // summation's 16 lanes of a row read 4 columns from each of the 4 weight
-    // blocks (unpadded, MT x 16 x 17 floats put them on the same banks).
-    constexpr int BSTRIDE = MT * 16 * DPAD + (16 - (MT * 16 * DPAD) % 64 + 64) % 64;
-    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][NB][BSTRIDE];
-    static_assert(NB * BSTRIDE * 4 >= 16 * 16 * 16, "transpose slot fits a wave's part");
+    // each wave's partial rows of C: row m (of 16 MT) holds the slice's
+    // DSPLIT_ROWS columns at a pitch of DROW floats, so that a lane's 4
+    // consecutive columns of one block leave as one 16-byte write and the
+    // summation reads 16 bytes per wave (written as single floats, the
+    // reduction took ~1 us at M = 64).  The 272-byte pitch puts the 16 rows
+    // one write instruction covers on different banks.  During the main loop
+    // each wave's part holds its transpose slot.
+    constexpr int DROW = DSPLIT_ROWS + 4;
+    constexpr int PWORDS = 16 * MT * DROW > 1024 ? 16 * MT * DROW : 1024;
+    __shared__ __attribute__((aligned(16))) float part[DECODE_WAVES][PWORDS];
+    static_assert(PWORDS * 4 >= 16 * 16 * 16, "transpose slot fits a wave's part");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     unsigned long long t_start = 0, t_land = 0;
     if (p.rec && tid == 0) t_start = __builtin_amdgcn_s_memrealtime();
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
     const int kb1 = s0 + (wave + 1) * (s1 - s0) / DECODE_WAVES;
     const int lr = lane >> 4, lu = lane & 15;  // load layout: row within 4, 16-byte unit
     const int orow = lane & 15, ochunk = lane >> 4;  // operand layout: row, 8-element chunk
-    u32x4* slot = (u32x4*)&part[wave][0][0];
+    u32x4* slot = (u32x4*)&part[wave][0];
 
     f32x4 acc[NB][MT];
 #pragma unroll
@@ -340,14 +343,13 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) mma_chunk<DT>(acc[b][mt], wf[b], xf[mt]);
     }
-    // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each block
+    // lane holds C^T rows n = 4 (lane / 16) + e, column m = lane % 16 of each
+    // block: columns 16 b + 4 (lane / 16) .. + 3 of row 16 mt + lane % 16
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                part[wave][b][mt * 16 * DPAD + (4 * (lane >> 4) + e) * DPAD + (lane & 15)] = acc[b][mt][e];
+            *(f32x4*)&part[wave][(mt * 16 + (lane & 15)) * DROW + b * 16 + 4 * (lane >> 4)] = acc[b][mt];
     __syncthreads();
     unsigned long long t_loop = 0;
     if (p.rec && tid == 0) t_loop = __builtin_amdgcn_s_memrealtime();
@@ -357,12 +359,10 @@ __global__ __launch_bounds__(DECODE_WAVES * 64) void gemm_decode_split_kernel(De
     float* ws = p.ws + (int64_t)ks * p.M * p.N + n0;
     for (int t = tid; t < 16 * p.M; t += DECODE_WAVES * 64) {
         const int m = t >> 4, q = t & 15;
-        const int b = q >> 2, mt = m >> 4, ml = m & 15;
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        // the waves' partials added in wave order
+        f32x4 sum = *(const f32x4*)&part[0][m * DROW + 4 * q];
 #pragma unroll
-        for (int w = 0; w < DECODE_WAVES; ++w)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) sum[c] += part[w][b][mt * 16 * DPAD + (4 * (q & 3) + c) * DPAD + ml];
+        for (int w = 1; w < DECODE_WAVES; ++w) sum += *(const f32x4*)&part[w][m * DROW + 4 * q];
         *(f32x4*)(ws + (int64_t)m * p.N + 4 * q) = sum;
     }
     if (p.rec && tid == 0) {
