@@ -475,6 +475,21 @@ def bench_streamk(dge, torch, steps):
     return out
 
 
+def bench_square256(dge, inputs, torch, steps):
+    """The 256^3 fp16 correctness configuration (uniform inputs, fp32 out):
+    launch-bound, so its time is reported and no roofline fraction claimed;
+    per call from host-launched windows and from graph replays."""
+    A, B = inputs.square256()
+    dA, dB = _dev(A, "f16", torch), _dev(B, "f16", torch)
+    C = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+    fn = lambda: dge.gemm_ex(dA, dB, C, out_dtype=torch.float32)
+    te = time_leg(fn, steps, torch, warm_seconds=0.1)
+    tg = time_graph(fn, steps, torch, warm_seconds=0.1)
+    return {"us_host_launched": te["us"], "us_graph": tg["us"],
+            "TFLOPs_graph": gemm_flops(256, 256, 256) / tg["us"] / 1e6,
+            "timing": te, "graph_timing": tg}
+
+
 def bench_library_context(dge, torch, steps):
     """Context only: torch.matmul (the vendor BLAS, hipBLASLt on ROCm) on the
     4096^3 fp16 product, K x N and N x K B, beside this library's gemm_f16 on
@@ -921,6 +936,7 @@ def main():
         line["decode_4096"] = bench_decode(dge, inputs, torch, extra_steps, peaks)
         line["fp32_ladder"] = bench_ladder(dge, inputs, torch, extra_steps)
         line["library_context"] = bench_library_context(dge, torch, extra_steps)
+        line["square256_f32out"] = bench_square256(dge, inputs, torch, extra_steps)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(A, B, inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
