@@ -160,6 +160,27 @@ def test_split_k_exact_and_deterministic(splits, trans_b):
     assert_close(C, Tg, Ug, what="split gelu")
 
 
+# more slices than the fixup adds per batch of loads (8): 11 and 20 slices
+# of K = 1280, integer inputs, the bias and beta applied in the fixup
+@pytest.mark.parametrize("splits", [11, 20])
+def test_split_k_many_slices_with_bias_and_beta(splits):
+    M, N, K = 256, 384, 1280
+    A, B = _operands(M, N, K, "f16", False, True, 300 + splits)
+    r = np.random.Generator(np.random.PCG64(301 + splits))
+    bias = r.integers(-8, 9, N).astype(np.float64)
+    cold = r.integers(-64, 65, (M, N)).astype(np.float64)
+    T, _ = oracle.gemm(A, B, "f16", beta=2.0, C_old=cold, epi="bias", bias=bias)
+    ws = torch.empty(dge.gemm_workspace_size_splits(M, N, splits) // 4 + 1, dtype=torch.float32,
+                     device="cuda")
+    for out in (torch.float32, torch.float16):
+        C = torch.from_numpy(cold.astype(np.float32)).to(out).cuda()
+        dge.gemm_ex(to_dev(A, "f16"), to_dev(B, "f16"), C, beta=2.0, epi="bias",
+                    bias=to_dev(inputs.to_bits(bias, "f16"), "f16"), workspace=ws, algo="mfma",
+                    tile="128x128", splits=splits)
+        torch.cuda.synchronize()
+        assert_bits(C, T, what="splits=%d %s" % (splits, out))
+
+
 def test_split_request_without_workspace_is_an_error():
     A, B = _operands(64, 64, 512, "f16", False, False, 5)
     with pytest.raises(dge.GemmError) as e:
