@@ -100,6 +100,12 @@ def test_fp32_ladder_every_element(n):
         torch.cuda.synchronize()
         assert_close(C, T, U, what="n=%d %s" % (n, algo))
         del C
+    # with the workspace the library asks for (the schedule the benchmark
+    # times: a K split at n = 1024)
+    C = dge.gemm_ex(dA, dB, out_dtype=torch.float32, algo="mfma",
+                    workspace=_ws(n, n, n, torch.float32))
+    torch.cuda.synchronize()
+    assert_close(C, T, U, what="n=%d mfma with workspace" % n)
 
 
 # ------------------------------------------------------------ prefill, q4_0
