@@ -190,7 +190,7 @@ def _strip_comments(src):
 # the files that define the headline kernel (a committed traffic summary is
 # only used while they are unchanged)
 HEADLINE_KERNEL_FILES = ("device_common.h", "mfma_gemm.h", "mfma_direct.h", "mfma_instances.inc",
-                         "kernels_direct_f16.hip")
+                         "kernels_direct_f16_nn.hip")
 
 
 def _src_hash(files=HEADLINE_KERNEL_FILES):

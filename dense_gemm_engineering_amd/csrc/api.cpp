@@ -413,11 +413,12 @@ gemm_status_t launch_status(hipError_t e) {
 
 // direct: 0 = register-staged kernel only, 1 = direct-to-LDS kernel when the
 // problem qualifies (full tiles, 16-bit inputs, aligned operands).
-// The direct-to-LDS kernels address each load as a wave-uniform base plus a
-// 32-bit per-lane byte offset of up to 32 rows: leading dimensions below 2^24
-// elements keep it under 2^31.
+// The direct-to-LDS kernels address each load, and each 16-bit output store,
+// as a wave-uniform base plus a 32-bit per-lane byte offset of up to 32 rows:
+// leading dimensions below 2^24 elements keep it under 2^31.
 bool direct_ld_ok(const Gemm& g) {
-    return g.lda < ((int64_t)1 << 24) && (g.b_q4 || g.ldb < ((int64_t)1 << 24));
+    return g.lda < ((int64_t)1 << 24) && (g.b_q4 || g.ldb < ((int64_t)1 << 24)) &&
+           g.ldc < ((int64_t)1 << 24);
 }
 
 // Tiles whose stream-K schedule can run this problem: the direct-to-LDS

@@ -20,10 +20,13 @@ LIB = os.path.join(PKG, "libdge_gemm.so")
 LIB_DIAG = os.path.join(PKG, "libdge_gemm_diag.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["api.cpp", "kernels_mfma_f16.hip", "kernels_mfma_bf16.hip", "kernels_mfma_f32.hip",
-           "kernels_direct_f16.hip", "kernels_direct_bf16.hip",
-           "kernels_misc.hip", "kernels_skinny.hip", "kernels_skinny_fold.hip", "kernels_q4.hip",
-           "kernels_decode.hip", "kernels_probe.hip"]
+# the longest compiles first, so the parallel build's wall time is the
+# longest unit's rather than a long unit started last
+SOURCES = ["kernels_direct_f16_nn.hip", "kernels_direct_f16_nt.hip", "kernels_direct_bf16_nn.hip",
+           "kernels_direct_bf16_nt.hip", "kernels_q4.hip", "kernels_skinny.hip",
+           "kernels_skinny_fold.hip", "kernels_mfma_f16.hip", "kernels_mfma_bf16.hip",
+           "kernels_mfma_f32.hip", "kernels_decode.hip", "kernels_misc.hip", "kernels_probe.hip",
+           "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -58,17 +61,16 @@ def build(jobs=None, verbose=False, diag=True):
     """Compile and link libdge_gemm.so (and, with diag, libdge_gemm_diag.so)."""
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(OBJDIR + "_diag", exist_ok=True)
-    work = [(s, False) for s in SOURCES] + ([(s, True) for s in SOURCES] if diag else [])
+    work = [(s, d) for s in SOURCES for d in ((False, True) if diag else (False,))]
     jobs = jobs or min(len(work), max(1, len(os.sched_getaffinity(0))), 16)
     with ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(_compile, work))
     for _, errs in results:
         if errs and verbose:
             print(errs, file=sys.stderr)
-    n = len(SOURCES)
-    _link([o for o, _ in results[:n]], LIB)
+    _link([o for (o, _), (_, d) in zip(results, work) if not d], LIB)
     if diag:
-        _link([o for o, _ in results[n:]], LIB_DIAG)
+        _link([o for (o, _), (_, d) in zip(results, work) if d], LIB_DIAG)
     return LIB
 
 

@@ -67,12 +67,22 @@ template <> struct OutType<OUT_F16> {
     typedef _Float16 T;
     __device__ static inline _Float16 from_f32(float x) { return (_Float16)x; }
     __device__ static inline float to_f32(_Float16 x) { return (float)x; }
+    // two values rounded to nearest-even and packed, a in the low half: one
+    // v_cvt_pk_f16_f32
+    __device__ static inline uint32_t pack2(float a, float b) {
+        typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, (v2){(_Float16)a, (_Float16)b});
+    }
 };
 template <> struct OutType<OUT_BF16> {
     static constexpr int BYTES = 2;
     typedef __bf16 T;
     __device__ static inline __bf16 from_f32(float x) { return (__bf16)x; }
     __device__ static inline float to_f32(__bf16 x) { return (float)x; }
+    __device__ static inline uint32_t pack2(float a, float b) {
+        typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, (v2){(__bf16)a, (__bf16)b});
+    }
 };
 
 // tanh form of GELU: 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))), in fp32.

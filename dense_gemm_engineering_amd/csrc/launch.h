@@ -47,10 +47,22 @@ hipError_t launch_mfma_f32(int tile, int trans_b, int fast, const MfmaArgs& a, i
 // Returns hipErrorInvalidValue for a tile it does not provide.
 // sk = 1: the persistent stream-K schedule, nwg = its grid (a.sk_* set, the
 // arrival counters zeroed on the same stream first).
-hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, int sk,
-                                  hipStream_t s);
-hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg, int sk,
-                                   hipStream_t s);
+// One entry per input type and B layout (nn: K x N, nt: N x K), each built in
+// a translation unit of its own.
+hipError_t launch_mfma_direct_f16_nn(int tile, const MfmaArgs& a, int nwg, int sk, hipStream_t s);
+hipError_t launch_mfma_direct_f16_nt(int tile, const MfmaArgs& a, int nwg, int sk, hipStream_t s);
+hipError_t launch_mfma_direct_bf16_nn(int tile, const MfmaArgs& a, int nwg, int sk, hipStream_t s);
+hipError_t launch_mfma_direct_bf16_nt(int tile, const MfmaArgs& a, int nwg, int sk, hipStream_t s);
+inline hipError_t launch_mfma_direct_f16(int tile, int trans_b, const MfmaArgs& a, int nwg, int sk,
+                                         hipStream_t s) {
+    return trans_b ? launch_mfma_direct_f16_nt(tile, a, nwg, sk, s)
+                   : launch_mfma_direct_f16_nn(tile, a, nwg, sk, s);
+}
+inline hipError_t launch_mfma_direct_bf16(int tile, int trans_b, const MfmaArgs& a, int nwg, int sk,
+                                          hipStream_t s) {
+    return trans_b ? launch_mfma_direct_bf16_nt(tile, a, nwg, sk, s)
+                   : launch_mfma_direct_bf16_nn(tile, a, nwg, sk, s);
+}
 // Fused q4-weight GEMM (p.B = q4 blocks of an N x K weight, 4-byte aligned;
 // K % 64 == 0; full tiles of the given shape only).
 hipError_t launch_mfma_q4_f16(int tile, const MfmaArgs& a, int nwg, hipStream_t s);

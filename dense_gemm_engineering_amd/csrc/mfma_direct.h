@@ -248,7 +248,15 @@ template <int MS> struct TLayout;
 template <> struct TLayout<16> { static constexpr int NG = 1, CG = 0; };
 template <> struct TLayout<32> { static constexpr int NG = 4, CG = 8; };
 
-template <int DT, int OT, int MS, int WTM, int WTN, int TM, int TN, int IP>
+// Epilogue modes, fixed per instance so that no work of an unused option is
+// done: the flags are uniform, but left to the compiler the per-element
+// branches become selects, and every element then pays for the GELU, the
+// beta term and the bias whether asked for or not (and with a run-time beta
+// each group's old values are waited for one load at a time).  Bits: alpha
+// and bias, GELU, beta; no bit set = the accumulator as it is.
+enum : int { EM_PLAIN = 0, EM_AFFINE = 1, EM_GELU = 2, EM_BETA = 4 };
+
+template <int DT, int OT, int EM, int MS, int WTM, int WTN, int TM, int TN, int IP>
 __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
     const MfmaArgs& p, typename AccBlock<MS>::T (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0,
     int wm0, int wn0, int lane) {
@@ -258,8 +266,9 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
     // the lane's bias values: held in registers when few (16 for the 8-wave
     // tile), else loaded per group of 4 columns (the 4-wave tiles keep 256
     // accumulators live)
-    constexpr bool PRE_BIAS = TN * NG * 4 <= 16;
-    const bool has_bias = p.ep.epi != EPI_NONE;
+    constexpr bool PRE_BIAS = EM != EM_PLAIN && TN * NG * 4 <= 16;
+    const bool has_bias = EM != EM_PLAIN && p.ep.epi != EPI_NONE;
+    constexpr bool beta = (EM & EM_BETA) != 0;
     float bias[PRE_BIAS ? TN : 1][PRE_BIAS ? NG : 1][4];
     if constexpr (PRE_BIAS) {
 #pragma unroll
@@ -271,11 +280,15 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
                     bias[j][g][e] =
                         has_bias ? load_elem<DT>(p.ep.bias, n0 + wn0 + MS * j + CG * g + cl + e) : 0.0f;
     }
-    const bool gelu = p.ep.epi == EPI_BIAS_GELU, beta = p.ep.beta != 0.0f;
     auto finish4 = [&](int i, int j, int g, float* t) __attribute__((always_inline)) {
+        if constexpr (EM == EM_PLAIN) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = acc[i][j][4 * g + e];
+            return;
+        }
         const int64_t row = m0 + wm0 + MS * i + rl, col = n0 + wn0 + MS * j + CG * g + cl;
         float old[4] = {0.f, 0.f, 0.f, 0.f};
-        if (beta) {
+        if constexpr (beta) {
             const T* c = (const T*)p.C + row * p.ldc + col;
 #pragma unroll
             for (int e = 0; e < 4; ++e) old[e] = OutType<OT>::to_f32(c[e]);
@@ -283,12 +296,12 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v = p.ep.alpha * acc[i][j][4 * g + e];
-            if (beta) v += p.ep.beta * old[e];
+            if constexpr (beta) v += p.ep.beta * old[e];
             if constexpr (PRE_BIAS)
                 v += bias[j][g][e];
             else if (has_bias)
                 v += load_elem<DT>(p.ep.bias, col + e);
-            t[e] = gelu ? gelu_tanh(v) : v;
+            t[e] = (EM & EM_GELU) ? gelu_tanh(v) : v;
         }
     };
     if constexpr (OT == OUT_F32) {
@@ -318,10 +331,8 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
                     for (int g = 0; g < NG; ++g) {
                         float t[4];
                         finish4(i, j, g, t);
-                        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[0])) |
-                                            ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[1])) << 16);
-                        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[2])) |
-                                            ((uint32_t)__builtin_bit_cast(uint16_t, OutType<OT>::from_f32(t[3])) << 16);
+                        const uint32_t lo = OutType<OT>::pack2(t[0], t[1]);
+                        const uint32_t hi = OutType<OT>::pack2(t[2], t[3]);
                         const int r = MS * (i - i0) + rl;
                         const int cb = (MS * j + CG * g + cl) * 2;  // byte column in the row
                         *(DGE_LDS u32x2*)(stg + r * RB + (((cb >> 4) ^ (r & (CPR - 1))) << 4) + (cb & 15)) =
@@ -329,16 +340,31 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
                     }
             DGE_DIAG_SYNC();
             // this wave's rows back as 16-byte pieces (the wave's own LDS
-            // operations complete in order: no barrier)
+            // operations complete in order: no barrier); each store addresses
+            // a wave-uniform row base plus a 32-bit lane offset (leading
+            // dimensions are below 2^24, so 16 rows stay far below 2^32)
+            const uint32_t loff = (uint32_t)(((lane / CPR) * p.ldc + n0 + wn0 + 8 * (lane % CPR)) * 2);
 #pragma unroll
             for (int q = 0; q < IP * MS * CPR / 64; ++q) {
                 const int r = q * (64 / CPR) + lane / CPR, ch = lane % CPR;
                 const u32x4 v = *(const DGE_LDS u32x4*)(stg + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
-                T* c = (T*)p.C + (int64_t)(m0 + wm0 + MS * i0 + r) * p.ldc + n0 + wn0 + 8 * ch;
-                __builtin_nontemporal_store(v, (u32x4*)c);
+                const char* rb = (const char*)p.C + (int64_t)(m0 + wm0 + MS * i0 + q * (64 / CPR)) * p.ldc * 2;
+                __builtin_nontemporal_store(v, (u32x4*)(rb + loff));
             }
         }
     }
+}
+
+template <int DT, int EM, int MS, int WTM, int WTN, int TM, int TN, int IP>
+__device__ __attribute__((always_inline)) inline void epilogue_tile_t_em(
+    const MfmaArgs& p, typename AccBlock<MS>::T (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0,
+    int wm0, int wn0, int lane) {
+    if (p.c_type == OUT_F16)
+        epilogue_tile_t_ot<DT, OUT_F16, EM, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    else if (p.c_type == OUT_BF16)
+        epilogue_tile_t_ot<DT, OUT_BF16, EM, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    else
+        epilogue_tile_t_ot<DT, OUT_F32, EM, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
 }
 
 // STG: LDS bytes the staging may use (it starts at stg_all); each wave gets
@@ -372,12 +398,20 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t(
         return;
     }
     DGE_LDS char* stg = stg_all + wave * PER_WAVE;
-    if (p.c_type == OUT_F16)
-        epilogue_tile_t_ot<DT, OUT_F16, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
-    else if (p.c_type == OUT_BF16)
-        epilogue_tile_t_ot<DT, OUT_BF16, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
-    else
-        epilogue_tile_t_ot<DT, OUT_F32, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    constexpr int AB = EM_AFFINE | EM_BETA;
+    const bool gelu = p.ep.epi == EPI_BIAS_GELU;
+    if (p.ep.beta != 0.0f) {
+        if (gelu)
+            epilogue_tile_t_em<DT, AB | EM_GELU, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        else
+            epilogue_tile_t_em<DT, AB, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    } else if (gelu) {
+        epilogue_tile_t_em<DT, EM_AFFINE | EM_GELU, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    } else if (p.ep.epi != EPI_NONE || p.ep.alpha != 1.0f) {
+        epilogue_tile_t_em<DT, EM_AFFINE, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    } else {
+        epilogue_tile_t_em<DT, EM_PLAIN, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+    }
 }
 
 template <int DT, int BM, int BN, int WM, int WN, bool TRANS_B, int MS, bool Q4 = false,
@@ -739,10 +773,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     // flight.  Ends with every load landed and both buffers free.
     // Prologue: stages 0 and 1 in flight, wait for stage 0, read its k-block 0.
     auto mainloop = [&](int nk, int par, bool pre) __attribute__((always_inline)) {
+    // (zeroed accumulators are pinned ahead of the first wait below: left
+    // alone the compiler sinks the moves behind it, so they run after the
+    // data has landed instead of while it is in flight; 8-wave tiles only,
+    // whose accumulators sit in VGPRs)
     if (!pre) issue_part(par, 0, 0, NDMA);
     if constexpr (Q4 && !Q4_3) q4_load(0);
     issue_part(par ^ 1, nk > 1 ? 1 : 0, 0, NP0);
     if constexpr (Q4 && !Q4_3) q4_store(par);
+    if constexpr (NW == 8 && MS == 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((NP0 & 15) | ((NP0 >> 4) << 14)));  // vmcnt(NP0)
     __syncthreads();
     if constexpr (Q4 && !Q4_3) q4_load(nk > 1 ? 1 : 0);
@@ -830,6 +874,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     issue_part(0, 0, 0, NDMA);
     issue_part(1, nk > 1 ? 1 : nk - 1, 0, NDMA);
     issue_part(2, nk > 2 ? 2 : nk - 1, 0, NDMA);
+    if constexpr (NW == 8 && MS == 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70 | (((2 * NDMA) & 15) | (((2 * NDMA) >> 4) << 14)));  // vmcnt(2 NDMA)
     __syncthreads();
     read_kblock(0, 0, fa[0], fb[0]);

@@ -253,7 +253,8 @@ gemm_status_t prefill_q4_f16(int64_t M, int64_t N, int64_t K, const void* A, int
  * same binary16 values dequant_q4_f16 writes, so the result equals
  * prefill_q4_f16's up to the GEMM's own summation order.  The fused kernel
  * takes shapes whose M and N are multiples of a 128 x 64 (or larger) tile,
- * K % 64 == 0, q 4-byte aligned and A, C 16-byte aligned with lda % 8 == 0;
+ * K % 64 == 0, q 4-byte aligned, A, C 16-byte aligned with lda % 8 == 0
+ * and lda, ldc below 2^24;
  * the workspace then only serves a K split (gemm_workspace_size with
  * GEMM_IN_F16 gives its size; less workspace = no split).  Any other shape
  * expands the weights into the workspace first, which must then hold

@@ -427,7 +427,9 @@ def test_skinny_bias_in_accumulators(M, N, K, trans_b):
 def test_direct_lds_path_epilogue_every_output(out, trans_b, dtype):
     # the direct kernels' register epilogue (each lane: 4 consecutive
     # columns of a row; 16-bit outputs repacked through the wave's LDS):
-    # alpha, beta reading C, bias and GELU for every tile and output type
+    # alpha, beta reading C, bias and GELU for every tile and output type,
+    # in each of the kernel's compiled epilogue forms (accumulator as is;
+    # alpha and bias; with GELU; with beta; with beta and GELU)
     M, N, K = 512, 512, 256
     A, B = _operands(M, N, K, dtype, trans_b, False, 900)
     r = np.random.Generator(np.random.PCG64(901))
@@ -436,16 +438,17 @@ def test_direct_lds_path_epilogue_every_output(out, trans_b, dtype):
     out_name = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}[out]
     cold_bits = inputs.to_bits(r.uniform(-1, 1, (M, N)), out_name)
     cold = oracle.decode(cold_bits, out_name)
-    for epi, beta in (("bias_gelu", -0.5), ("bias", 0.0), ("none", 1.0)):
+    for epi, alpha, beta in (("bias_gelu", 0.75, -0.5), ("bias_gelu", 1.0, 0.0), ("bias", 0.75, 0.0),
+                             ("bias", 1.0, 1.0), ("none", 0.75, 1.0), ("none", 1.0, 0.0)):
         b = bias if epi != "none" else None
-        T, U = oracle.gemm(A, B, dtype, trans_b=trans_b, alpha=0.75, beta=beta, C_old=cold,
+        T, U = oracle.gemm(A, B, dtype, trans_b=trans_b, alpha=alpha, beta=beta, C_old=cold,
                            epi=epi, bias=b)
         for tile in DIRECT_TILES:
             if tile == "128x64" and not trans_b:
                 continue  # runs the register-staged kernel
             C = to_dev(cold_bits, out_name)
-            dge.gemm_ex(to_dev(A, dtype), to_dev(B, dtype), C, trans_b=trans_b, alpha=0.75,
+            dge.gemm_ex(to_dev(A, dtype), to_dev(B, dtype), C, trans_b=trans_b, alpha=alpha,
                         beta=beta, epi=epi, bias=to_dev(bias_bits, dtype) if b is not None else None,
                         algo="mfma_direct", tile=tile, splits=1)
             torch.cuda.synchronize()
-            assert_close(C, T, U, 0.75, what="%s %s beta=%g" % (tile, epi, beta))
+            assert_close(C, T, U, alpha, what="%s %s alpha=%g beta=%g" % (tile, epi, alpha, beta))
