@@ -236,11 +236,12 @@ __device__ inline void q4_decode4(uint32_t nib, h2v d2, uint32_t* o) {
 // MS j + CG g + 4 (l / MS) (MS = 16: one group, CG unused; MS = 32: four
 // groups, CG = 8), accumulator elements 4 g .. 4 g + 3.  alpha, beta (4
 // consecutive old values), bias, GELU and the rounding run in registers;
-// 16-bit results go through the wave's own part of LDS (IP row blocks at a
-// time, 16-byte chunks XOR-swizzled by row) and leave as 16-byte row
-// pieces: no workgroup barrier.  fp32 results and split-K partials leave
-// straight from registers, 16 bytes per lane.  Full tiles, 16-byte aligned
-// rows.  The final C stores are non-temporal (streamed towards memory rather
+// the results go through the wave's own part of LDS (IP row blocks at a
+// time, 16-byte chunks XOR-swizzled by row) and leave as 16-byte pieces of
+// whole rows of the wave tile: no workgroup barrier.  (fp32 results stored
+// straight from registers left as 64-byte row pieces, and drained slower.)
+// Split-K partials leave straight from registers, 16 bytes per lane.  Full
+// tiles, 16-byte aligned rows.  The final C stores are non-temporal (streamed towards memory rather
 // than left dirty in L2 for the end-of-kernel write-back: 4096^3 NN 113.1 ->
 // 111.5 us, NT 113.0 -> 108.7 us, 4096 x 4096 x 256 21.5 -> 19.6 us);
 // split-K partials, which the fixup reads back, are ordinary stores.
@@ -256,7 +257,7 @@ template <> struct TLayout<32> { static constexpr int NG = 4, CG = 8; };
 // and bias, GELU, beta; no bit set = the accumulator as it is.
 enum : int { EM_PLAIN = 0, EM_AFFINE = 1, EM_GELU = 2, EM_BETA = 4 };
 
-template <int DT, int OT, int EM, int MS, int WTM, int WTN, int TM, int TN, int IP>
+template <int DT, int OT, int EM, int MS, int WTM, int WTN, int TM, int TN, int PW>
 __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
     const MfmaArgs& p, typename AccBlock<MS>::T (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0,
     int wm0, int wn0, int lane) {
@@ -304,67 +305,59 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t_ot(
             t[e] = (EM & EM_GELU) ? gelu_tanh(v) : v;
         }
     };
-    if constexpr (OT == OUT_F32) {
+    // the wave's staging (PW bytes) holds IP row blocks of its tile at a time
+    constexpr int EB = OutType<OT>::BYTES;
+    constexpr int RB = WTN * EB;   // bytes of a staged row
+    constexpr int CPR = RB / 16;   // 16-byte chunks per row (a power of two)
+    constexpr int IP0 = PW / (MS * RB);
+    constexpr int IP = IP0 >= TM ? TM : (IP0 >= 4 ? 4 : (IP0 >= 2 ? 2 : 1));
+    static_assert(IP0 >= 1, "a row block of the wave tile fits the staging");
+    static_assert((CPR & (CPR - 1)) == 0 && CPR >= 4 && TM % IP == 0, "staging layout");
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+    for (int i0 = 0; i0 < TM; i0 += IP) {
+#pragma unroll
+        for (int i = i0; i < i0 + IP; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
                     float t[4];
                     finish4(i, j, g, t);
-                    float* c = (float*)p.C + (int64_t)(m0 + wm0 + MS * i + rl) * p.ldc + n0 + wn0 +
-                               MS * j + CG * g + cl;
-                    __builtin_nontemporal_store((f32x4){t[0], t[1], t[2], t[3]}, (f32x4*)c);
+                    const int r = MS * (i - i0) + rl;
+                    const int cb = (MS * j + CG * g + cl) * EB;  // byte column in the row
+                    DGE_LDS char* d = stg + r * RB + (((cb >> 4) ^ (r & (CPR - 1))) << 4) + (cb & 15);
+                    if constexpr (EB == 4)
+                        *(DGE_LDS f32x4*)d = (f32x4){t[0], t[1], t[2], t[3]};
+                    else
+                        *(DGE_LDS u32x2*)d = (u32x2){OutType<OT>::pack2(t[0], t[1]),
+                                                     OutType<OT>::pack2(t[2], t[3])};
                 }
-    } else {
-        constexpr int RB = WTN * 2;    // bytes of a staged row
-        constexpr int CPR = RB / 16;   // 16-byte chunks per row (a power of two)
-        static_assert((CPR & (CPR - 1)) == 0 && CPR >= 4 && TM % IP == 0, "staging layout");
+        DGE_DIAG_SYNC();
+        // this wave's rows back as 16-byte pieces (the wave's own LDS
+        // operations complete in order: no barrier); each store addresses
+        // a wave-uniform row base plus a 32-bit lane offset (leading
+        // dimensions are below 2^24, so 16 rows stay below 2^31)
+        const uint32_t loff = (uint32_t)(((lane / CPR) * p.ldc + n0 + wn0) * EB + 16 * (lane % CPR));
 #pragma unroll
-        for (int i0 = 0; i0 < TM; i0 += IP) {
-#pragma unroll
-            for (int i = i0; i < i0 + IP; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) {
-                        float t[4];
-                        finish4(i, j, g, t);
-                        const uint32_t lo = OutType<OT>::pack2(t[0], t[1]);
-                        const uint32_t hi = OutType<OT>::pack2(t[2], t[3]);
-                        const int r = MS * (i - i0) + rl;
-                        const int cb = (MS * j + CG * g + cl) * 2;  // byte column in the row
-                        *(DGE_LDS u32x2*)(stg + r * RB + (((cb >> 4) ^ (r & (CPR - 1))) << 4) + (cb & 15)) =
-                            (u32x2){lo, hi};
-                    }
-            DGE_DIAG_SYNC();
-            // this wave's rows back as 16-byte pieces (the wave's own LDS
-            // operations complete in order: no barrier); each store addresses
-            // a wave-uniform row base plus a 32-bit lane offset (leading
-            // dimensions are below 2^24, so 16 rows stay far below 2^32)
-            const uint32_t loff = (uint32_t)(((lane / CPR) * p.ldc + n0 + wn0 + 8 * (lane % CPR)) * 2);
-#pragma unroll
-            for (int q = 0; q < IP * MS * CPR / 64; ++q) {
-                const int r = q * (64 / CPR) + lane / CPR, ch = lane % CPR;
-                const u32x4 v = *(const DGE_LDS u32x4*)(stg + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
-                const char* rb = (const char*)p.C + (int64_t)(m0 + wm0 + MS * i0 + q * (64 / CPR)) * p.ldc * 2;
-                __builtin_nontemporal_store(v, (u32x4*)(rb + loff));
-            }
+        for (int q = 0; q < IP * MS * CPR / 64; ++q) {
+            const int r = q * (64 / CPR) + lane / CPR, ch = lane % CPR;
+            const u32x4 v = *(const DGE_LDS u32x4*)(stg + r * RB + ((ch ^ (r & (CPR - 1))) << 4));
+            const char* rb = (const char*)p.C + (int64_t)(m0 + wm0 + MS * i0 + q * (64 / CPR)) * p.ldc * EB;
+            __builtin_nontemporal_store(v, (u32x4*)(rb + loff));
         }
     }
 }
 
-template <int DT, int EM, int MS, int WTM, int WTN, int TM, int TN, int IP>
+template <int DT, int EM, int MS, int WTM, int WTN, int TM, int TN, int PW>
 __device__ __attribute__((always_inline)) inline void epilogue_tile_t_em(
     const MfmaArgs& p, typename AccBlock<MS>::T (&acc)[TM][TN], DGE_LDS char* stg, int m0, int n0,
     int wm0, int wn0, int lane) {
     if (p.c_type == OUT_F16)
-        epilogue_tile_t_ot<DT, OUT_F16, EM, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_ot<DT, OUT_F16, EM, MS, WTM, WTN, TM, TN, PW>(p, acc, stg, m0, n0, wm0, wn0, lane);
     else if (p.c_type == OUT_BF16)
-        epilogue_tile_t_ot<DT, OUT_BF16, EM, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_ot<DT, OUT_BF16, EM, MS, WTM, WTN, TM, TN, PW>(p, acc, stg, m0, n0, wm0, wn0, lane);
     else
-        epilogue_tile_t_ot<DT, OUT_F32, EM, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_ot<DT, OUT_F32, EM, MS, WTM, WTN, TM, TN, PW>(p, acc, stg, m0, n0, wm0, wn0, lane);
 }
 
 // STG: LDS bytes the staging may use (it starts at stg_all); each wave gets
@@ -377,9 +370,6 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t(
     static_assert(TM * MS == WTM && TN * MS == WTN, "wave tile");
     constexpr int NG = TLayout<MS>::NG, CG = TLayout<MS>::CG;
     constexpr int PER_WAVE = STG / (WM * WN);
-    constexpr int IP0 = PER_WAVE / (MS * WTN * 2);
-    constexpr int IP = IP0 >= TM ? TM : (IP0 >= 4 ? 4 : (IP0 >= 2 ? 2 : 1));
-    static_assert(IP0 >= 1, "a row block of the wave tile fits the staging");
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
     if (p.ws) {  // split-K partial sums: fp32, no epilogue
@@ -402,15 +392,15 @@ __device__ __attribute__((always_inline)) inline void epilogue_tile_t(
     const bool gelu = p.ep.epi == EPI_BIAS_GELU;
     if (p.ep.beta != 0.0f) {
         if (gelu)
-            epilogue_tile_t_em<DT, AB | EM_GELU, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+            epilogue_tile_t_em<DT, AB | EM_GELU, MS, WTM, WTN, TM, TN, PER_WAVE>(p, acc, stg, m0, n0, wm0, wn0, lane);
         else
-            epilogue_tile_t_em<DT, AB, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+            epilogue_tile_t_em<DT, AB, MS, WTM, WTN, TM, TN, PER_WAVE>(p, acc, stg, m0, n0, wm0, wn0, lane);
     } else if (gelu) {
-        epilogue_tile_t_em<DT, EM_AFFINE | EM_GELU, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_em<DT, EM_AFFINE | EM_GELU, MS, WTM, WTN, TM, TN, PER_WAVE>(p, acc, stg, m0, n0, wm0, wn0, lane);
     } else if (p.ep.epi != EPI_NONE || p.ep.alpha != 1.0f) {
-        epilogue_tile_t_em<DT, EM_AFFINE, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_em<DT, EM_AFFINE, MS, WTM, WTN, TM, TN, PER_WAVE>(p, acc, stg, m0, n0, wm0, wn0, lane);
     } else {
-        epilogue_tile_t_em<DT, EM_PLAIN, MS, WTM, WTN, TM, TN, IP>(p, acc, stg, m0, n0, wm0, wn0, lane);
+        epilogue_tile_t_em<DT, EM_PLAIN, MS, WTM, WTN, TM, TN, PER_WAVE>(p, acc, stg, m0, n0, wm0, wn0, lane);
     }
 }
 
