@@ -749,7 +749,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_direct_kernel(MfmaArgs p
     constexpr int DPART = Q4 ? 1 : (KB - 1 < 3 ? KB - 1 : 3);
     constexpr int NP0 = NDMA / DPART;                    // loads in the first part
     // MFMAs of a stage's last k-block left after the barrier (measured, same
-    // box, alternating processes): the 256 x 256 8-wave tile runs 4096^3 in
+    // machine, alternating processes): the 256 x 256 8-wave tile runs 4096^3 in
     // 105.7 us with 24 of its 32 after the barrier against 112.3 with 8 (NN;
     // NT 110.5 -> 104.5); the 256 x 128 8-wave tile with three LDS stages
     // runs best with all 16 after it (2048 x 4096 x 11008: 153.3 us with 4,

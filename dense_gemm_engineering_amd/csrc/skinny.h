@@ -39,7 +39,7 @@
 //    instances carrying only that epilogue); pairs are converted with one
 //    packed instruction; and a wave whose rows are one contiguous block of
 //    C stores it at a uniform base plus a 32-bit offset.  N = 160: 14.1 ->
-//    12.4 us (graph replays, HBM-cold X and C, same box, alternating
+//    12.4 us (graph replays, HBM-cold X and C, same machine, alternating
 //    processes).
 #pragma once
 
